@@ -1,0 +1,106 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention-forward library.
+ *
+ * One operation: the forward pass of multi-head scaled-dot-product attention,
+ *   O = softmax(Q K^T * scale + mask) V          per (sequence, head),
+ * the definition of mlqm.cn/news/343191 chapter 1, fused into one kernel as
+ * the chain "Q K^T -> scale -> mask -> softmax -> P V" of the same page's
+ * §3.1, computed tile by tile with the online softmax of
+ * jianying88.com/news/49672 §3 (running row maximum m_i and exponential sum
+ * l_i), so the S x S score matrix never reaches device memory.
+ *
+ * All tensor pointers are DEVICE pointers owned by the caller. The library
+ * allocates no memory, keeps no mutable global state and never synchronizes
+ * the stream (except attn_check_cu_seqlens), so it is reentrant and
+ * thread-safe. Work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream).
+ */
+#ifndef SDPA08_ATTN_H
+#define SDPA08_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out. */
+enum {
+  ATTN_DTYPE_FP16 = 0, /* IEEE binary16 */
+  ATTN_DTYPE_BF16 = 1  /* bfloat16 */
+};
+
+/* Status codes. Argument errors are returned before any HIP call is made. */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,       /* B, H or S out of range, or sizes overflow */
+  ATTN_ERR_DTYPE = -3,       /* dtype is not ATTN_DTYPE_FP16 / ATTN_DTYPE_BF16 */
+  ATTN_ERR_SCALE = -4,       /* scale is NaN or infinite */
+  ATTN_ERR_UNSUPPORTED = -5, /* head dimension D is not 64 or 128 */
+  ATTN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
+  ATTN_ERR_SEQLENS = -7,     /* cu_seqlens failed validation (debug check) */
+  ATTN_ERR_ALIGN = -8        /* a tensor pointer is not 16-byte aligned */
+};
+
+/*
+ * attn_fwd -- fused attention forward.
+ *
+ * Padded mode (cu_seqlens == NULL):
+ *   q, k, v, out : contiguous (B, S, H, D) arrays of `dtype`
+ *                  (the (batch, seq, head, dim) layout of
+ *                  jianying88.com/news/49672 §4.2).
+ *   lse          : contiguous (B, H, S) float32, or NULL (not written).
+ * Packed mode (cu_seqlens != NULL), the variable-length interface of
+ * lnrk.cn/news/11729 §1 with separate q, k, v tensors:
+ *   B            : number of sequences; S: total token count T.
+ *   q, k, v, out : contiguous (T, H, D) arrays of `dtype`.
+ *   cu_seqlens   : int32 DEVICE array of B+1 prefix offsets, cu_seqlens[0]=0,
+ *                  non-decreasing, cu_seqlens[B]=T (zero-length sequences
+ *                  allowed). Its contents are a precondition; set the
+ *                  environment variable ATTN_DEBUG=1 to validate them (this
+ *                  synchronizes the stream) before the launch.
+ *   lse          : contiguous (H, T) float32, or NULL.
+ *
+ * Semantics: self-attention (query and key lengths equal, same head count
+ * for Q and K/V). Scores s_ij = scale * <q_i, k_j> accumulate in fp32 from
+ * fp16/bf16 operands; with causal != 0 key j is visible to query i iff j <= i
+ * (indices local to the sequence; mlqm.cn/news/343191 §3.1). Packed
+ * sequences never attend to each other. lse[i] = ln(sum_j exp(s_ij)) over the
+ * visible keys (natural log, fp32). out is rounded to nearest-even.
+ *   D     : 64 or 128, else ATTN_ERR_UNSUPPORTED.
+ *   scale : any finite float (0 gives uniform attention; negative allowed);
+ *           callers usually pass 1/sqrt(D).
+ *   B, H, S : 1 <= H <= 65535, B >= 1 (padded) or >= 0 (packed), S >= 0;
+ *           B*H*S*D must fit in int64 and the grid in 2^31-1 workgroups.
+ *           S == 0 (or B == 0 in packed mode) is a valid no-op.
+ * q, k, v, out must be 16-byte aligned (lse: 4-byte aligned), else
+ * ATTN_ERR_ALIGN. out/lse must not overlap q, k, v or each other.
+ *
+ * Errors: ATTN_ERR_* argument codes are returned synchronously with nothing
+ * enqueued; ATTN_ERR_LAUNCH if the launch fails (hipGetLastError).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int S, int D, int causal, float scale, int dtype,
+             const int32_t* cu_seqlens, void* stream);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* attn_strerror(int status);
+
+/*
+ * attn_check_cu_seqlens -- debug validator of packed-mode offsets.
+ * Copies cu_seqlens (B+1 int32, device) to the host on `stream`,
+ * synchronizes it and checks cu[0] == 0, cu non-decreasing, cu[B] == T.
+ * Returns ATTN_OK, ATTN_ERR_SEQLENS, ATTN_ERR_NULL / ATTN_ERR_SHAPE for bad
+ * arguments, or ATTN_ERR_LAUNCH if the copy fails.
+ */
+int attn_check_cu_seqlens(const int32_t* cu_seqlens, int B, int T, void* stream);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA08_ATTN_H */

@@ -1,0 +1,133 @@
+"""ctypes binding of the C ABI in include/attn.h (argument marshalling only).
+
+Every step of the attention forward runs in the HIP library; this module
+only turns torch tensors into device pointers, sizes and a stream handle.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+ATTN_DTYPE_FP16 = 0
+ATTN_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
+    -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
+    -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN",
+}
+EXPORTS = ("attn_fwd", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP attention library not built: {p} "
+                           "(run python -m scaled_dot_product_08_amd.build)")
+    lib = ctypes.CDLL(p)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_check_cu_seqlens.restype = ctypes.c_int
+    lib.attn_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_version.restype = ctypes.c_int
+    lib.attn_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def attn_version() -> int:
+    return load_library().attn_version()
+
+
+def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
+                 cu_ptr, stream_ptr) -> int:
+    """Direct call with integer pointers; returns the status code."""
+    return load_library().attn_fwd(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
+                                   int(D), int(causal), float(scale), int(dtype), cu_ptr, stream_ptr)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_DTYPE_FP16
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None,
+             cu_seqlens=None, stream=None) -> None:
+    """Call attn_fwd on torch device tensors.
+
+    Padded: q,k,v,out (B,S,H,D), lse (B,H,S) fp32 or None.
+    Packed: q,k,v,out (T,H,D), cu_seqlens int32 (nseq+1,), lse (H,T) or None.
+    ``scale=None`` means 1/sqrt(D) rounded to float32.
+    """
+    for t in (q, k, v, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if cu_seqlens is None:
+        B, S, H, D = q.shape
+        cu_ptr = None
+    else:
+        T, H, D = q.shape
+        B, S = cu_seqlens.numel() - 1, T
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      None if lse is None else lse.data_ptr(), B, H, S, D, int(bool(causal)),
+                      scale, _dtype_code(q), cu_ptr, _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+
+
+def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
+        with_lse: bool = True, stream=None):
+    """Allocate O (and LSE) with torch and run attn_fwd. Returns (O, LSE or None)."""
+    import torch
+    out = torch.empty_like(q)
+    lse = None
+    if with_lse:
+        if cu_seqlens is None:
+            B, S, H, _ = q.shape
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+        else:
+            T, H, _ = q.shape
+            lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, out, lse, causal=causal, scale=scale, cu_seqlens=cu_seqlens, stream=stream)
+    return out, lse
+
+
+def check_cu_seqlens(cu_seqlens, T: int, stream=None) -> int:
+    return load_library().attn_check_cu_seqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                                                int(T), _stream_ptr(stream))

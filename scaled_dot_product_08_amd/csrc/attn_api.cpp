@@ -1,0 +1,134 @@
+// C ABI of the attention-forward library: argument validation, kernel
+// instance selection, grid sizing and launch on the caller's stream.
+// Validation is pure host logic and returns before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "attn_kernel.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool debug_enabled() {
+  const char* e = std::getenv("ATTN_DEBUG");
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
+// Validation shared by attn_fwd; no HIP call. Fills the grid size on success.
+int validate(const void* q, const void* k, const void* v, void* out, const float* lse, int B,
+             int H, int S, int D, float scale, int dtype, const int32_t* cu, long long* grid) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  const bool packed = cu != nullptr;
+  if (H < 1 || H > 65535 || S < 0) return ATTN_ERR_SHAPE;
+  if (packed ? (B < 0) : (B < 1)) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  // Element count must fit in int64 (it always does for int inputs, but the
+  // product of four ints is checked explicitly).
+  const long double elems = (long double)(packed ? 1 : B) * S * H * D;
+  if (elems > (long double)LLONG_MAX / 2) return ATTN_ERR_SHAPE;
+  const long long bm = sdpa08::query_tile_rows();
+  long long tiles;
+  if (packed) {
+    tiles = (long long)S / bm + B;                // virtual tiles of the packed batch
+    *grid = tiles * H;
+  } else {
+    tiles = ((long long)S + bm - 1) / bm;
+    *grid = tiles * B * H;
+  }
+  if (*grid > INT_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return kVersion; }
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "B, H or S out of range (or the problem is too large)";
+    case ATTN_ERR_DTYPE: return "unknown dtype (expected ATTN_DTYPE_FP16 or ATTN_DTYPE_BF16)";
+    case ATTN_ERR_SCALE: return "scale is not finite";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension (expected 64 or 128)";
+    case ATTN_ERR_LAUNCH: return "HIP runtime error at launch";
+    case ATTN_ERR_SEQLENS: return "cu_seqlens is not a valid prefix-offset array";
+    case ATTN_ERR_ALIGN: return "tensor pointer misaligned (q/k/v/out need 16 bytes, lse 4)";
+    default: return "unknown status";
+  }
+}
+
+int attn_check_cu_seqlens(const int32_t* cu_seqlens, int B, int T, void* stream) {
+  if (cu_seqlens == nullptr) return ATTN_ERR_NULL;
+  if (B < 0 || T < 0) return ATTN_ERR_SHAPE;
+  std::vector<int32_t> h((size_t)B + 1);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess) {
+    return ATTN_ERR_LAUNCH;
+  }
+  if (hipStreamSynchronize(st) != hipSuccess) return ATTN_ERR_LAUNCH;
+  if (h[0] != 0 || h[B] != T) return ATTN_ERR_SEQLENS;
+  for (int i = 0; i < B; ++i) {
+    if (h[i + 1] < h[i]) return ATTN_ERR_SEQLENS;
+  }
+  return ATTN_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+             int S, int D, int causal, float scale, int dtype, const int32_t* cu_seqlens,
+             void* stream) {
+  long long grid = 0;
+  const int st = validate(q, k, v, out, lse, B, H, S, D, scale, dtype, cu_seqlens, &grid);
+  if (st != ATTN_OK) return st;
+  const bool packed = cu_seqlens != nullptr;
+  if (S == 0 || (packed && B == 0)) return ATTN_OK;
+  if (packed && debug_enabled()) {
+    const int c = attn_check_cu_seqlens(cu_seqlens, B, S, stream);
+    if (c != ATTN_OK) return c;
+  }
+  sdpa08::FwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.S = S;
+  const long long bm = sdpa08::query_tile_rows();
+  p.n_qtiles = packed ? (int)((long long)S / bm + B) : (int)(((long long)S + bm - 1) / bm);
+  const float log2e = 1.4426950408889634f;
+  if (scale > 0.0f) {
+    p.c_log2 = scale * log2e;
+    p.q_mode = 0;
+  } else if (scale < 0.0f) {
+    p.c_log2 = -scale * log2e;
+    p.q_mode = 1;
+  } else {
+    p.c_log2 = log2e;
+    p.q_mode = 2;
+  }
+  const hipError_t e = sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
+                                          (unsigned)grid, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa08 {
+
+struct FwdParams {
+  const uint16_t* q;        // (B,S,H,D) or (T,H,D), 16-bit elements
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;               // (B,H,S) or (H,T) fp32, may be null
+  const int32_t* cu_seqlens;  // packed mode only (device)
+  int B;                    // batch (padded) or number of sequences (packed)
+  int H;
+  int S;                    // sequence length (padded) or total tokens T (packed)
+  int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed)
+  float c_log2;             // |scale| * log2(e), or log2(e) when scale == 0
+  int q_mode;               // 0: scale > 0, 1: scale < 0 (use -Q), 2: scale == 0 (Q := 0)
+};
+
+// Rows of the query tile one workgroup owns.
+int query_tile_rows();
+
+// Launch the kernel instance for (D, dtype, causal, packed) on `stream`.
+hipError_t launch_fwd(const FwdParams& p, int D, bool bf16, bool causal, bool varlen,
+                      unsigned grid, hipStream_t stream);
+
+}  // namespace sdpa08

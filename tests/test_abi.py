@@ -1,0 +1,69 @@
+"""The C ABI library loads, exports every declared symbol and validates arguments on the host.
+
+Nothing here launches a kernel: every call below is rejected (or is a no-op)
+before the library makes any HIP call, so it runs on a CPU-only machine.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scaled_dot_product_08_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    assert set(_declared_functions()) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_strerror(lib):
+    assert binding.attn_version() >= 10000
+    for code, name in binding.STATUS.items():
+        assert binding.attn_strerror(code)
+    assert binding.attn_strerror(12345) == "unknown status"
+
+
+P = 1 << 20   # a 16-byte-aligned fake device address (never dereferenced)
+
+
+def call(q=P, k=P, v=P, o=P, lse=None, B=1, H=2, S=128, D=64, causal=0, scale=0.125,
+         dtype=binding.ATTN_DTYPE_FP16, cu=None):
+    return binding.attn_fwd_raw(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, cu, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(dtype=2), -3), (dict(dtype=-1), -3),
+    (dict(D=96), -5), (dict(D=256), -5), (dict(D=0), -5),
+    (dict(scale=float("nan")), -4), (dict(scale=float("inf")), -4), (dict(scale=-float("inf")), -4),
+    (dict(H=0), -2), (dict(H=70000), -2), (dict(B=0), -2), (dict(S=-1), -2), (dict(B=-1, cu=P), -2),
+    (dict(q=P + 8), -8), (dict(o=P + 2), -8), (dict(lse=P + 2), -8),
+    (dict(B=4096, H=4096, S=1 << 30), -2),
+])
+def test_argument_errors(kw, code):
+    assert call(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(S=0), dict(B=0, S=0, cu=P), dict(B=0, S=100, cu=P)])
+def test_empty_problems_are_noops(kw):
+    # Returns before any HIP call: nothing to compute.
+    assert call(**kw) == 0
