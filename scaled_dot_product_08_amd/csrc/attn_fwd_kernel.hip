@@ -287,8 +287,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
         m_run = m_new;
       }
 
-      // P = exp2(s * c - m), packed to 16 bit; l sums the packed values.
+      // P = exp2(s * c - m), packed to 16 bit for P V.
+      // l: bf16 keeps 8 significant bits, so a row with few visible keys
+      // would carry up to 2^-9 relative error into ln(l) if l summed the
+      // rounded values; it sums the fp32 values instead. fp16 (11 bits) keeps
+      // that error below 2.5e-4 and sums the rounded pairs with one dot2.
       uint32_t pk[2][8];
+      float tile_l = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -296,9 +301,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_log2, -m_run));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_log2, -m_run));
           pk[kb][t] = pack2<BF16>(e0, e1);
-          l_run = add_pair<BF16>(pk[kb][t], l_run);
+          if constexpr (BF16) {
+            tile_l += e0 + e1;
+          } else {
+            tile_l = add_pair<false>(pk[kb][t], tile_l);
+          }
         }
       }
+      l_run += tile_l;
 
       // O^T += V^T P^T over four 16-key steps.
       const int vrow = swap23(li);
