@@ -2,31 +2,36 @@
 //
 // One workgroup of 4 waves (256 lanes) owns a tile of BM = 128 query rows of
 // one (sequence, head); wave w owns rows 32w..32w+31 of the tile. The kernel
-// streams the visible keys in tiles of BN = 64 rows through double-buffered
-// LDS and, per tile, runs the fused chain of mlqm.cn/news/343191 §3.1
+// streams the visible keys in tiles of BN = 64 rows through a two-stage LDS
+// ring and, per tile, runs the fused chain of mlqm.cn/news/343191 §3.1
 // (Q K^T -> scale -> mask -> softmax -> P V) with the online softmax of
 // jianying88.com/news/49672 §3: a running row maximum m and exponential sum l
 // per query row, so no score ever leaves registers.
 //
+// Data movement:
+//   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16
+//     bytes per lane): no registers, no LDS store instructions. Each 16-byte
+//     chunk of a row is placed at chunk ^ swz(row), which makes every LDS
+//     access pattern below conflict-free on the 64-bank LDS.
+//   * Rows past the end of a sequence come back as zeros from the buffer
+//     descriptor's range check, so ragged tails need no branches.
+//
 // Orientation (what makes the softmax cheap on a 64-lane wave):
 //   * Scores are produced transposed, S^T = K Q^T, by v_mfma_f32_32x32x16
-//     with A = a 32-key block of K (from LDS) and B = Q^T (registers). The
-//     accumulator column index is the lane (mod 32), so each lane holds one
-//     query row and 16 of its 32 keys; the other 16 sit in lane ^ 32. A row
-//     max / sum is 15 in-lane ops plus one exchange with lane ^ 32.
+//     with A = a 32-key block of K (ds_read_b128) and B = Q^T (registers).
+//     The accumulator column index is the lane (mod 32), so each lane holds
+//     one query row and 16 of its 32 keys; the other 16 sit in lane ^ 32.
 //   * The output is accumulated transposed too, O^T += V^T P^T, with B = the
 //     probabilities straight out of the score accumulator (cast to 16 bit)
-//     and A = V^T read from LDS. Each lane again owns one query row, so the
-//     rescale by exp(m_old - m_new) is a per-lane scalar.
-//   * V is transposed once per tile on its way into LDS (in registers), and
-//     its key columns and head-dim rows are permuted so that every MFMA
-//     operand is one 16-byte LDS read and every O store is 16 bytes.
+//     and A = V^T read from the row-major V tile by the transposing LDS read
+//     ds_read_b64_tr_b16. Each lane owns one query row, so rescaling the
+//     accumulator is a per-lane scalar multiply.
 //
 // Exponentials use exp2 on logits pre-multiplied by scale*log2(e). The row
 // maximum is refreshed lazily: the stale maximum is kept until the new one
-// exceeds it by more than 2^8 (probabilities are then at most 256, exact in
-// the normalisation because the same maximum enters numerator and
-// denominator), which saves most of the accumulator rescales.
+// exceeds it by more than 8 (log2 units; probabilities are then at most 256,
+// and the same maximum enters numerator and denominator), which skips most
+// accumulator rescales.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,12 +46,20 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BM = 128;       // query rows per workgroup
 constexpr int BN = 64;        // keys per LDS tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
+constexpr int HEAD_GROUP = 2; // heads whose query tiles are interleaved on one XCD
+constexpr int NXCD = 8;       // accelerator complex dies; workgroups go round-robin over them
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
+constexpr int BUF_FLAGS = 0x00020000;   // raw buffer descriptor word 3 (32-bit dwords)
 
 // 32x32x16 MFMA, fp32 accumulate; a/b carry eight 16-bit values each.
 template <bool BF16>
@@ -71,63 +84,86 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
-// acc + lo(p) + hi(p): sums the 16-bit probabilities exactly as they enter P V.
-template <bool BF16>
-__device__ __forceinline__ float add_pair(uint32_t p, float acc) {
-  if constexpr (BF16) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
-  } else {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
-  }
+// acc + lo(p) + hi(p) for a pair of fp16 values (one v_dot2).
+__device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
 }
 
-// Swap bits 2 and 3 of a small index. Used twice:
-//  * V^T column of key j inside a 64-key tile, so that the eight keys one
-//    lane contributes to a P V step are adjacent;
-//  * V^T row read by MFMA row p, so that each lane ends up with runs of
-//    eight consecutive head-dim outputs.
+// Swap bits 2 and 3 of a small index (orders head-dim outputs so that every
+// lane ends with runs of eight consecutive columns).
 __device__ __forceinline__ int swap23(int j) {
   return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// 16-byte chunk swizzle of an LDS tile row. Chunk c of row r lives at
+// chunk c ^ swz(r). Chosen so that (a) 16 consecutive rows read at one
+// logical chunk hit 16 different bank groups (K operand reads) and (b) 4
+// consecutive rows read over 64 contiguous bytes hit 16 different bank
+// groups (transposing V reads), on 64 banks x 4 bytes.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // vmcnt(0), other counters untouched (gfx9 encoding).
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
-  constexpr int KSTR = D + 8;          // K tile row stride in LDS (elements)
-  constexpr int VSTR = BN + 8;         // V^T tile row stride in LDS (elements)
-  constexpr int DCH = D / 16;          // 16-deep contraction chunks of Q K^T
-  constexpr int DB = D / 32;           // 32-row blocks of O^T
-  constexpr int KCH = D / 8;           // 16-byte chunks per K/V row
-  constexpr int K_LD = BN * KCH / NTHREADS;   // K chunks per lane per tile
-  constexpr int KG = (D == 128) ? 4 : 2;      // keys per lane in the V transpose
-  static_assert((BN / KG) * KCH == NTHREADS, "V transpose mapping must cover the tile");
+  constexpr int ROWB = D * 2;                  // bytes per K/V row
+  constexpr int TILEB = BN * ROWB;             // bytes per K (or V) tile
+  constexpr int STAGEB = 2 * TILEB;            // K tile + V tile
+  constexpr int LDW = TILEB / 1024 / NWAVES;   // 1 KB direct loads per wave per tile
+  constexpr int DCH = D / 16;                  // 16-deep contraction chunks of Q K^T
+  constexpr int DB = D / 32;                   // 32-row blocks of O^T
+  static_assert(LDW >= 1, "tile must give every wave a 1 KB load");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D * VSTR];
+  // Two separate arrays, one per stage: the compiler can then tell that LDS
+  // reads of one stage never alias the in-flight direct loads into the other
+  // and does not wait for those loads before every read.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int li = lane & 31;     // query row inside the wave's 32 / MFMA row
+  const int li = lane & 31;     // query row inside the wave / MFMA row index
   const int hh = lane >> 5;     // which half of the contraction this lane feeds
 
   // ---- which (sequence, head, query tile) this workgroup owns -------------
-  // Linear id: the query-tile rank is the slowest index and is taken in
-  // reverse, so the longest causal tiles start first; (batch, head) is the
-  // fastest index, so consecutive workgroups (which land on different XCDs)
-  // carry different heads and every query tile of one head lands on the
-  // same XCD whenever the head count is a multiple of 8.
+  // Workgroup i runs on XCD i % 8. Undo that interleave so each XCD owns a
+  // contiguous run of the logical order, then walk heads in groups of
+  // HEAD_GROUP with the query tiles of a group interleaved, longest (causal)
+  // tiles first. An XCD then works on a few heads at a time, whose K/V stay
+  // in its L2, and the longest tiles start first.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % NXCD;
+  const int local = blockIdx.x / NXCD;
+  const int gq = G / NXCD, gr = G % NXCD;
+  const int logical = (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
   const int nbh = VARLEN ? p.H : p.B * p.H;
-  const int rank = blockIdx.x / nbh;
-  const int bh = blockIdx.x - rank * nbh;
+  const int nt = p.n_qtiles;
+  const int grp = logical / (HEAD_GROUP * nt);
+  const int in_grp = min(HEAD_GROUP, nbh - grp * HEAD_GROUP);
+  const int rem = logical - grp * (HEAD_GROUP * nt);
+  const int rank = rem / in_grp;
+  const int bh = grp * HEAD_GROUP + (rem - rank * in_grp);
   const int h = bh % p.H;
   const int b = VARLEN ? 0 : bh / p.H;
-  const int vt = p.n_qtiles - 1 - rank;
+  const int vt = nt - 1 - rank;
   int seq_start = 0, L = p.S, q0;
   if constexpr (VARLEN) {
     // Virtual tile space: sequence s owns tiles [cu[s]/BM + s, ... + ceil(L_s/BM)).
@@ -145,78 +181,84 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     q0 = vt * BM;
   }
 
-  const size_t tok_stride = (size_t)p.H * D;
-  const size_t base = ((size_t)b * p.S + seq_start) * tok_stride + (size_t)h * D;
-  const uint16_t* __restrict__ qg = p.q + base;
-  const uint16_t* __restrict__ kg = p.k + base;
-  const uint16_t* __restrict__ vg = p.v + base;
-  uint16_t* __restrict__ og = p.o + base;
+  const uint32_t tok_bytes = (uint32_t)p.H * ROWB;             // bytes between tokens
+  const size_t base = (((size_t)b * p.S + seq_start) * p.H + h) * D;   // elements
+  const uint16_t* qg = p.q + base + (size_t)q0 * p.H * D;
+  const uint16_t* kg = p.k + base;
+  const uint16_t* vg = p.v + base;
+  uint16_t* og = p.o + base + (size_t)q0 * p.H * D;
 
   const int kv_end = CAUSAL ? min(q0 + BM, L) : L;
   const int n_kv = (kv_end + BN - 1) / BN;
   const int wq0 = q0 + wave * 32;        // first query row of this wave
   const int qi = wq0 + li;               // this lane's query row
+  const uint32_t q_rows = (uint32_t)min(L - q0, BM);
 
   // ---- Q^T operand, resident in registers for the whole key loop ----------
-  // Rows past the sequence end load the last row instead (never stored).
-  const int qi_ld = min(qi, L - 1);
+  // Rows past the sequence end read as zeros (buffer range check).
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qg, q_rows * tok_bytes);
+  const uint32_t q_voff = (uint32_t)(wave * 32 + li) * tok_bytes + hh * 16;
+  // Sign handling of the scale: negative scale uses -Q and |scale|; zero
+  // scale zeroes Q so every visible score is exactly 0.
+  const uint32_t q_xor = (p.q_mode == 1) ? 0x80008000u : 0u;
+  const uint32_t q_and = (p.q_mode == 2) ? 0u : 0xffffffffu;
   u32x4 qreg[DCH];
 #pragma unroll
   for (int c = 0; c < DCH; ++c) {
-    qreg[c] = *reinterpret_cast<const u32x4*>(qg + (size_t)qi_ld * tok_stride + c * 16 + hh * 8);
-    if (p.q_mode == 1) qreg[c] ^= 0x80008000u;          // negative scale: use -Q, |scale|
-    else if (p.q_mode == 2) qreg[c] = u32x4{0u, 0u, 0u, 0u};  // zero scale: all scores 0
+    qreg[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_voff + c * 32, 0, 0));
   }
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) qreg[c] = (qreg[c] ^ q_xor) & q_and;
   const float c_log2 = p.c_log2;          // |scale| * log2(e) (> 0)
 
-  // ---- K / V tile staging ---------------------------------------------------
-  u32x4 kpre[K_LD];
-  u32x4 vpre[KG];
-  const int v_grp = tid / KCH;           // key group (KG keys) of this lane
-  const int v_dc = tid - v_grp * KCH;    // 8-wide head-dim chunk of this lane
+  // ---- per-lane constant offsets --------------------------------------------
+  // Direct loads: load u of this wave fills LDS bytes [(wave*LDW+u)*1 KB, +1 KB)
+  // of a tile; lane l writes 16 bytes at +16 l, i.e. row r, physical chunk pc,
+  // and so fetches logical chunk pc ^ swz(r) of key row r.
+  uint32_t ld_voff[LDW];
+#pragma unroll
+  for (int u = 0; u < LDW; ++u) {
+    const int byte = (wave * LDW + u) * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    ld_voff[u] = (uint32_t)r * tok_bytes + (uint32_t)((pc ^ swz<D>(r)) * 16);
+  }
+  // K operand: row li (+32 for the second key block), logical chunk 2c+hh.
+  uint32_t k_off[DCH];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) k_off[c] = li * ROWB + (((2 * c + hh) ^ swz<D>(li)) << 4);
+  // V^T operand via the transposing read: in each 16-lane block, lane s points
+  // at key row (s / 4) of a 4-key group and at a 4-column group; the read
+  // hands lane i the 4 keys of column (group(i/4) + i%4). Column groups are
+  // ordered so that output rows come out as runs of 8 consecutive columns.
+  uint32_t v_off[2][DB];
+  {
+    const int blk = li >> 4, s = li & 15;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int key = t2 * 8 + hh * 4 + (s >> 2);        // + 16 * (16-key step)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = db * 32 + blk * 16 + swap23(4 * (s & 3));
+        v_off[t2][db] = key * ROWB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) * 2));
+      }
+    }
+  }
 
-  auto load_tile = [&](int j) {
+  // Issue the direct loads of key tile j into stage `st`.
+  auto issue_tile = [&](int j, int st) {
     const int key0 = j * BN;
+    const uint32_t rows = (uint32_t)min(L - key0, BN);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
+    uint8_t* kdst = (st ? smem1 : smem0) + wave * LDW * 1024;
+    uint8_t* vdst = kdst + TILEB;
 #pragma unroll
-    for (int u = 0; u < K_LD; ++u) {
-      const int c = tid + u * NTHREADS;
-      const int row = c / KCH, col = (c - row * KCH) * 8;
-      const int r = min(key0 + row, L - 1);
-      kpre[u] = *reinterpret_cast<const u32x4*>(kg + (size_t)r * tok_stride + col);
+    for (int u = 0; u < LDW; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < KG; ++u) {
-      const int row = v_grp * KG + u;
-      const int r = min(key0 + row, L - 1);
-      vpre[u] = *reinterpret_cast<const u32x4*>(vg + (size_t)r * tok_stride + v_dc * 8);
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < K_LD; ++u) {
-      const int c = tid + u * NTHREADS;
-      const int row = c / KCH, col = (c - row * KCH) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][row * KSTR + col]) = kpre[u];
-    }
-    // Transpose KG keys x 8 dims into 8 rows of V^T (KG adjacent columns each).
-    const int col = swap23(v_grp * KG);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int w = dd >> 1;
-      const bool odd = dd & 1;
-      uint32_t pair[KG / 2];
-#pragma unroll
-      for (int u = 0; u < KG / 2; ++u) {
-        const uint32_t a = vpre[2 * u][w], c2 = vpre[2 * u + 1][w];
-        pair[u] = odd ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
-      }
-      uint16_t* dst = &vt_lds[buf][(v_dc * 8 + dd) * VSTR + col];
-      if constexpr (KG == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pair[0], pair[1]);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = pair[0];
-      }
+    for (int u = 0; u < LDW; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
     }
   };
 
@@ -227,130 +269,141 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   float m_run = -INFINITY;     // running max of the log2-scaled logits
   float l_run = 0.0f;          // this lane's half of the running exp-sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_kv; ++j) {
-    const int buf = j & 1;
+  auto compute_tile = [&](int j, const uint8_t* ks) {
+    const uint8_t* vs = ks + TILEB;
     const int key0 = j * BN;
-    if (j + 1 < n_kv) load_tile(j + 1);
-
     // A wave whose rows all precede the tile's first key has nothing to do.
-    const bool active = !CAUSAL || key0 <= wq0 + 31;
-    if (active) {
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16 s[2];
+    if (CAUSAL && key0 > wq0 + 31) return;
+
+    // S^T = K Q^T for two 32-key blocks.
+    f32x16 s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const uint16_t* krow = &k_lds[buf][(kb * 32 + li) * KSTR + hh * 8];
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < DCH; ++c) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + c * 16);
-          s[kb] = mfma32<BF16>(a, qreg[c], s[kb]);
-        }
+      for (int c = 0; c < DCH; ++c) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]);
+        s[kb] = mfma32<BF16>(a, qreg[c], s[kb]);
       }
+    }
 
-      // Mask keys past the sequence end and, under causality, keys after the
-      // query (only tiles that reach those positions pay for it).
-      const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            const bool ok = (key < L) && (!CAUSAL || key <= qi);
-            s[kb][r] = ok ? s[kb][r] : -INFINITY;
-          }
-        }
-      }
-
-      // Row maximum over this tile (16 + 16 values here, the rest in lane ^ 32).
-      float mx = s[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
-
-      // Lazy refresh of the running maximum.
-      const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
-      if (__builtin_amdgcn_ballot_w64(bump)) {
-        const float m_new = bump ? mx2 : m_run;
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-
-      // P = exp2(s * c - m), packed to 16 bit for P V.
-      // l: bf16 keeps 8 significant bits, so a row with few visible keys
-      // would carry up to 2^-9 relative error into ln(l) if l summed the
-      // rounded values; it sums the fp32 values instead. fp16 (11 bits) keeps
-      // that error below 2.5e-4 and sums the rounded pairs with one dot2.
-      uint32_t pk[2][8];
-      float tile_l = 0.0f;
+    // Mask keys past the sequence end and, under causality, keys after the
+    // query (only tiles that reach those positions pay for it).
+    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_log2, -m_run));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_log2, -m_run));
-          pk[kb][t] = pack2<BF16>(e0, e1);
-          if constexpr (BF16) {
-            tile_l += e0 + e1;
-          } else {
-            tile_l = add_pair<false>(pk[kb][t], tile_l);
-          }
-        }
-      }
-      l_run += tile_l;
-
-      // O^T += V^T P^T over four 16-key steps.
-      const int vrow = swap23(li);
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int kb = kc >> 1, e = kc & 1;
-        const u32x4 bop = {pk[kb][e * 4 + 0], pk[kb][e * 4 + 1], pk[kb][e * 4 + 2], pk[kb][e * 4 + 3]};
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(
-              &vt_lds[buf][(d * 32 + vrow) * VSTR + kc * 16 + hh * 8]);
-          acc[d] = mfma32<BF16>(a, bop, acc[d]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          const bool ok = (key < L) && (!CAUSAL || key <= qi);
+          s[kb][r] = ok ? s[kb][r] : -INFINITY;
         }
       }
     }
 
-    if (j + 1 < n_kv) store_tile(buf ^ 1);
+    // Row maximum over this tile (16 + 16 values here, the rest in lane ^ 32).
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
+
+    // Lazy refresh of the running maximum.
+    const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
+    if (__builtin_amdgcn_ballot_w64(bump)) {
+      const float m_new = bump ? mx2 : m_run;
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+
+    // P = exp2(s * c - m), packed to 16 bit for P V.
+    // l: bf16 keeps 8 significant bits, so a row with few visible keys would
+    // carry up to 2^-9 relative error into ln(l) if l summed the rounded
+    // values; it sums the fp32 values instead. fp16 (11 bits) keeps that
+    // error below 2.5e-4 and sums the rounded pairs with one dot2.
+    uint32_t pk[2][8];
+    float tile_l = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_log2, -m_run));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_log2, -m_run));
+        pk[kb][t] = pack2<BF16>(e0, e1);
+        if constexpr (BF16) {
+          tile_l += e0 + e1;
+        } else {
+          tile_l = add_pair_f16(pk[kb][t], tile_l);
+        }
+      }
+    }
+    l_run += tile_l;
+
+    // O^T += V^T P^T over four 16-key steps. Step (kb, e) uses score
+    // registers 8e..8e+7 of block kb, i.e. keys kb*32 + 16e + {0..3, 8..11}
+    // (+4 in the upper half-wave); the V reads fetch the same keys.
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int kb = kc >> 1, e = kc & 1;
+      const u32x4 bop = {pk[kb][e * 4 + 0], pk[kb][e * 4 + 1], pk[kb][e * 4 + 2], pk[kb][e * 4 + 3]};
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const uint8_t* vb = vs + kc * 16 * ROWB;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        acc[d] = mfma32<BF16>(a, bop, acc[d]);
+      }
+    }
+  };
+
+  // ---- main loop: two-stage LDS ring, unrolled by two ----------------------
+  issue_tile(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+#pragma unroll 1
+  for (int j = 0; j < n_kv; j += 2) {
+    if (j + 1 < n_kv) issue_tile(j + 1, 1);
+    compute_tile(j, smem0);
+    wait_vmem_all();
+    __syncthreads();
+    if (j + 1 >= n_kv) break;
+    if (j + 2 < n_kv) issue_tile(j + 2, 0);
+    compute_tile(j + 1, smem1);
+    wait_vmem_all();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = ln(l) + m -------------------------------
   const float l_tot = l_run + wave_xor32(l_run);
-  if (qi < L) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = og + (size_t)qi * tok_stride;
+  const float inv = 1.0f / l_tot;
+  // Stores past the sequence end fall outside the descriptor and are dropped.
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(og, q_rows * tok_bytes);
+  const uint32_t o_voff = (uint32_t)(wave * 32 + li) * tok_bytes + hh * 16;
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
+  for (int d = 0; d < DB; ++d) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 w;
+    for (int half = 0; half < 2; ++half) {
+      u32x4 w;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          w[t] = pack2<BF16>(acc[d][half * 8 + 2 * t] * inv, acc[d][half * 8 + 2 * t + 1] * inv);
-        }
-        *reinterpret_cast<u32x4*>(orow + d * 32 + half * 16 + hh * 8) = w;
+      for (int t = 0; t < 4; ++t) {
+        w[t] = pack2<BF16>(acc[d][half * 8 + 2 * t] * inv, acc[d][half * 8 + 2 * t + 1] * inv);
       }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), o_rsrc,
+                                             o_voff + (uint32_t)(d * 64 + half * 32), 0, 0);
     }
-    if (p.lse != nullptr && hh == 0) {
-      // __builtin_amdgcn_logf is the hardware base-2 logarithm.
-      const float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
-      p.lse[((size_t)b * p.H + h) * p.S + seq_start + qi] = lse;
-    }
+  }
+  if (p.lse != nullptr && hh == 0 && qi < L) {
+    // __builtin_amdgcn_logf is the hardware base-2 logarithm.
+    const float lse = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    p.lse[((size_t)b * p.H + h) * p.S + seq_start + qi] = lse;
   }
 }
 
