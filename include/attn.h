@@ -79,6 +79,10 @@ enum {
  *
  * Errors: ATTN_ERR_* argument codes are returned synchronously with nothing
  * enqueued; ATTN_ERR_LAUNCH if the launch fails (hipGetLastError).
+ *
+ * Tuning: the library picks 128- or 256-row query tiles per workgroup from
+ * the problem size; ATTN_WAVES=4 / ATTN_WAVES=8 forces 128 / 256 (results are
+ * bitwise identical either way).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int S, int D, int causal, float scale, int dtype,

@@ -40,7 +40,8 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
   // product of four ints is checked explicitly).
   const long double elems = (long double)(packed ? 1 : B) * S * H * D;
   if (elems > (long double)LLONG_MAX / 2) return ATTN_ERR_SHAPE;
-  const long long bm = sdpa08::query_tile_rows();
+  // The grid is largest with the smallest query tile; check that bound.
+  const long long bm = sdpa08::min_query_tile_rows();
   long long tiles;
   if (packed) {
     tiles = (long long)S / bm + B;                // virtual tiles of the packed batch
@@ -113,8 +114,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
   p.B = B;
   p.H = H;
   p.S = S;
-  const long long bm = sdpa08::query_tile_rows();
-  p.n_qtiles = packed ? (int)((long long)S / bm + B) : (int)(((long long)S + bm - 1) / bm);
+  p.n_qtiles = 0;   // set by the launcher for the workgroup size it picks
   const float log2e = 1.4426950408889634f;
   if (scale > 0.0f) {
     p.c_log2 = scale * log2e;
@@ -127,7 +127,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     p.q_mode = 2;
   }
   const hipError_t e = sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
-                                          (unsigned)grid, reinterpret_cast<hipStream_t>(stream));
+                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

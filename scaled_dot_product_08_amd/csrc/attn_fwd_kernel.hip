@@ -1,7 +1,7 @@
 // Fused attention forward for gfx950 (CDNA4): MFMA + LDS-tiled online softmax.
 //
-// One workgroup of 4 waves (256 lanes) owns a tile of BM = 128 query rows of
-// one (sequence, head); wave w owns rows 32w..32w+31 of the tile. The kernel
+// One workgroup of NW waves (NW = 4 or 8) owns a tile of BM = 32*NW query rows
+// of one (sequence, head); wave w owns rows 32w..32w+31 of the tile. The kernel
 // streams the visible keys in tiles of BN = 64 rows through a two-stage LDS
 // ring and, per tile, runs the fused chain of mlqm.cn/news/343191 §3.1
 // (Q K^T -> scale -> mask -> softmax -> P V) with the online softmax of
@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+
 #include "attn_kernel.h"
 
 namespace sdpa08 {
@@ -52,11 +54,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int BM = 128;       // query rows per workgroup
 constexpr int BN = 64;        // keys per LDS tile
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = NWAVES * 64;
-constexpr int HEAD_GROUP = 2; // heads whose query tiles are interleaved on one XCD
+constexpr int HEAD_GROUP = 4; // heads whose query tiles are interleaved on one XCD
 constexpr int NXCD = 8;       // accelerator complex dies; workgroups go round-robin over them
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 constexpr int BUF_FLAGS = 0x00020000;   // raw buffer descriptor word 3 (32-bit dwords)
@@ -121,8 +120,10 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) {
+  constexpr int NWAVES = NW;
+  constexpr int BM = 32 * NW;                  // query rows per workgroup
   constexpr int ROWB = D * 2;                  // bytes per K/V row
   constexpr int TILEB = BN * ROWB;             // bytes per K (or V) tile
   constexpr int STAGEB = 2 * TILEB;            // K tile + V tile
@@ -407,34 +408,61 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-static hipError_t launch_one(const FwdParams& p, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN>), dim3(grid), dim3(NTHREADS), 0,
-                     stream, p);
+// Workgroup size: 8 waves (256 query rows, one workgroup per CU) when the
+// problem has enough 256-row tiles to fill the chip several times over; else
+// 4 waves (128 rows, two workgroups per CU), which balances small problems
+// better. Both share every per-row arithmetic step, so results are identical.
+constexpr long long kBigProblemTiles = 4096;
+
+static int choose_waves(const FwdParams& p, bool varlen) {
+  // ATTN_WAVES=4 or 8 overrides the choice (used by tests to cover both).
+  if (const char* e = std::getenv("ATTN_WAVES")) {
+    if (e[0] == '4' && e[1] == '\0') return 4;
+    if (e[0] == '8' && e[1] == '\0') return 8;
+  }
+  const long long bh = varlen ? p.H : (long long)p.B * p.H;
+  const long long tiles256 = varlen ? (long long)p.S / 256 + p.B : ((long long)p.S + 255) / 256;
+  return tiles256 * bh >= kBigProblemTiles ? 8 : 4;
+}
+
+int max_query_tile_rows() { return 256; }
+int min_query_tile_rows() { return 128; }
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW>
+static hipError_t launch_one(FwdParams p, hipStream_t stream) {
+  constexpr long long BM = 32 * NW;
+  const long long tiles = VARLEN ? (long long)p.S / BM + p.B : ((long long)p.S + BM - 1) / BM;
+  p.n_qtiles = (int)tiles;
+  const long long grid = tiles * (VARLEN ? p.H : (long long)p.B * p.H);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool BF16>
-static hipError_t launch_d(const FwdParams& p, bool causal, bool varlen, unsigned grid,
-                           hipStream_t stream) {
-  if (causal) {
-    return varlen ? launch_one<D, BF16, true, true>(p, grid, stream)
-                  : launch_one<D, BF16, true, false>(p, grid, stream);
-  }
-  return varlen ? launch_one<D, BF16, false, true>(p, grid, stream)
-                : launch_one<D, BF16, false, false>(p, grid, stream);
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+static hipError_t launch_nw(const FwdParams& p, hipStream_t stream) {
+  return choose_waves(p, VARLEN) == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8>(p, stream)
+                                      : launch_one<D, BF16, CAUSAL, VARLEN, 4>(p, stream);
 }
 
-int query_tile_rows() { return BM; }
+template <int D, bool BF16>
+static hipError_t launch_d(const FwdParams& p, bool causal, bool varlen, hipStream_t stream) {
+  if (causal) {
+    return varlen ? launch_nw<D, BF16, true, true>(p, stream)
+                  : launch_nw<D, BF16, true, false>(p, stream);
+  }
+  return varlen ? launch_nw<D, BF16, false, true>(p, stream)
+                : launch_nw<D, BF16, false, false>(p, stream);
+}
 
 hipError_t launch_fwd(const FwdParams& p, int D, bool bf16, bool causal, bool varlen,
-                      unsigned grid, hipStream_t stream) {
+                      hipStream_t stream) {
   if (D == 64) {
-    return bf16 ? launch_d<64, true>(p, causal, varlen, grid, stream)
-                : launch_d<64, false>(p, causal, varlen, grid, stream);
+    return bf16 ? launch_d<64, true>(p, causal, varlen, stream)
+                : launch_d<64, false>(p, causal, varlen, stream);
   }
-  return bf16 ? launch_d<128, true>(p, causal, varlen, grid, stream)
-              : launch_d<128, false>(p, causal, varlen, grid, stream);
+  return bf16 ? launch_d<128, true>(p, causal, varlen, stream)
+              : launch_d<128, false>(p, causal, varlen, stream);
 }
 
 }  // namespace sdpa08

@@ -15,16 +15,18 @@ struct FwdParams {
   int B;                    // batch (padded) or number of sequences (packed)
   int H;
   int S;                    // sequence length (padded) or total tokens T (packed)
-  int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed)
+  int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed); set at launch
   float c_log2;             // |scale| * log2(e), or log2(e) when scale == 0
   int q_mode;               // 0: scale > 0, 1: scale < 0 (use -Q), 2: scale == 0 (Q := 0)
 };
 
-// Rows of the query tile one workgroup owns.
-int query_tile_rows();
+// Largest / smallest query tile (rows per workgroup) the launcher may pick.
+int max_query_tile_rows();
+int min_query_tile_rows();
 
-// Launch the kernel instance for (D, dtype, causal, packed) on `stream`.
+// Launch the kernel instance for (D, dtype, causal, packed) on `stream`; picks
+// the workgroup size, fills n_qtiles and sizes the grid.
 hipError_t launch_fwd(const FwdParams& p, int D, bool bf16, bool causal, bool varlen,
-                      unsigned grid, hipStream_t stream);
+                      hipStream_t stream);
 
 }  // namespace sdpa08

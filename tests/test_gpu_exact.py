@@ -14,16 +14,18 @@ pytestmark = pytest.mark.gpu
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_counts_and_constant_values_packed(D, dtype, causal):
+def test_counts_and_constant_values_packed(D, dtype, causal, waves, monkeypatch):
     """Q=K=0: every visible key has weight 1, so exp(LSE) is the count of visible keys and
     O equals the per-sequence constant V bit for bit; any cross-sequence leak breaks both."""
+    monkeypatch.setenv("ATTN_WAVES", waves)
     lens = [1, 5, 0, 64, 129, 300, 2, 1000, 77]
     cu = synth.cu_seqlens_of(lens)
     T, H = int(cu[-1]), 2
-    say(f"counts packed D={D} {dtype} causal={causal}")
+    say(f"counts packed D={D} {dtype} causal={causal} waves={waves}")
     q = torch.zeros((T, H, D), dtype=DT[dtype], device="cuda")
     k = torch.zeros_like(q)
     consts = np.repeat(np.arange(1, len(lens) + 1, dtype=np.float32), lens)
@@ -72,9 +74,11 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
 @pytest.mark.parametrize("packed", [False, True])
-def test_guard_bands_untouched(packed):
+def test_guard_bands_untouched(packed, waves, monkeypatch):
     """Sentinel regions around out and lse stay intact (no writes past the tensors)."""
+    monkeypatch.setenv("ATTN_WAVES", waves)
     G = 4096
     D, H = 128, 2
     if packed:

@@ -128,12 +128,19 @@ SHAPES = [
 ]
 
 
+@pytest.fixture(params=["4", "8"], ids=["bm128", "bm256"])
+def waves(request, monkeypatch):
+    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles."""
+    monkeypatch.setenv("ATTN_WAVES", request.param)
+    return int(request.param)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,S", SHAPES)
-def test_padded_shapes(B, H, S, D, dtype, causal):
-    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal}")
+def test_padded_shapes(B, H, S, D, dtype, causal, waves):
+    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal} waves={waves}")
     qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 1000 + S + D)
     check_full(qb, kb, vb, dtype, causal, scale_of(D))
 
@@ -141,8 +148,8 @@ def test_padded_shapes(B, H, S, D, dtype, causal):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_packed_shapes(D, dtype, causal):
-    lens = [1, 3, 0, 130, 257, 64, 0, 128, 200]
+def test_packed_shapes(D, dtype, causal, waves):
+    lens = [1, 3, 0, 130, 257, 64, 0, 128, 200, 513]
     cu = synth.cu_seqlens_of(lens)
     T = int(cu[-1])
     say(f"packed lens={lens} D={D} {dtype} causal={causal}")
@@ -164,6 +171,19 @@ def test_lse_optional():
     o2, l2 = run_padded(qb, kb, vb, "bf16", True, 0.1, with_lse=False)
     assert l2 is None
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("name", ["llama", "mha_causal"])
+def test_tile_size_choice_is_bitwise_neutral(name, monkeypatch):
+    """128- and 256-row query tiles give bitwise identical O and LSE (same per-row arithmetic)."""
+    cfg = synth.CONFIGS[name]
+    inp = synth.make_inputs(cfg, B=2 if cfg.B > 2 else cfg.B)
+    outs = []
+    for w in ("4", "8"):
+        monkeypatch.setenv("ATTN_WAVES", w)
+        o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
+        outs.append((o.cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
 def test_page_s2050_ragged_case():
