@@ -152,8 +152,8 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama", help="key of synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the B4 H12 S2048 D64 side figures")
@@ -183,7 +183,7 @@ def main():
     if not args.no_extra:
         for name in ("mha", "mha_causal"):
             c2 = synth.CONFIGS[name]
-            r2 = time_workload(c2, max(20, args.steps), args.warmup)
+            r2 = time_workload(c2, max(100, args.steps), max(100, args.warmup))
             also[name] = {"workload": c2.describe(), "us_per_call": round(r2["ms"] * 1e3, 2),
                           "tflops": round(r2["tflops"], 1),
                           "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4)}

@@ -37,6 +37,10 @@
 
 #include <cstdlib>
 
+#ifndef SDPA_SCHED_QK
+#define SDPA_SCHED_QK 1
+#endif
+
 #include "attn_kernel.h"
 
 namespace sdpa08 {
@@ -276,16 +280,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     // A wave whose rows all precede the tile's first key has nothing to do.
     if (CAUSAL && key0 > wq0 + 31) return;
 
-    // S^T = K Q^T for two 32-key blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    // S^T = K Q^T for two 32-key blocks. The two accumulation chains
+    // alternate (a chain's next MFMA waits for its previous result) and the
+    // K operands are read two contraction steps ahead of their MFMAs.
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      auto kread = [&](int kb, int c) {
+        return *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]);
+      };
+      u32x4 ka[2][2];
+      ka[0][0] = kread(0, 0);
+      ka[0][1] = kread(1, 0);
+      ka[1][0] = kread(0, 1);
+      ka[1][1] = kread(1, 1);
 #pragma unroll
       for (int c = 0; c < DCH; ++c) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]);
-        s[kb] = mfma32<BF16>(a, qreg[c], s[kb]);
+        s[0] = mfma32<BF16>(ka[c & 1][0], qreg[c], s[0]);
+        s[1] = mfma32<BF16>(ka[c & 1][1], qreg[c], s[1]);
+        if (c + 2 < DCH) {
+          ka[c & 1][0] = kread(0, c + 2);
+          ka[c & 1][1] = kread(1, c + 2);
+        }
       }
+#if SDPA_SCHED_QK
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int c = 0; c < DCH; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (c + 2 < DCH) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#endif
     }
 
     // Mask keys past the sequence end and, under causality, keys after the
