@@ -9,11 +9,14 @@ apart by their prefix offsets (lnrk.cn/news/11729 §1).
 import math
 
 
-def row(qrow, keys, vals, scale):
+def row(qrow, keys, vals, scale, biases=None):
     """Output and log-sum-exp of one query row against the list of visible keys."""
     logits = []
-    for kr in keys:
-        logits.append(scale * math.fsum(a * b for a, b in zip(qrow, kr)))
+    for n, kr in enumerate(keys):
+        x = scale * math.fsum(a * b for a, b in zip(qrow, kr))
+        if biases is not None:
+            x += biases[n]
+        logits.append(x)
     mx = max(logits)
     ws = [math.exp(x - mx) for x in logits]
     tot = math.fsum(ws)
@@ -50,4 +53,31 @@ def packed(q, k, v, cu, causal, scale):
                 keys = [k[j][h] for j in range(a, last + 1)]
                 vals = [v[j][h] for j in range(a, last + 1)]
                 O[i][h], L[h][i] = row(q[i][h], keys, vals, scale)
+    return O, L
+
+
+def sees(i, j, causal, window, n_global):
+    """Key j visible to query i (local indices): window of `window` keys ending at i
+    (|i - j| < window without causality); the first n_global rows see every key."""
+    if i < n_global:
+        return True
+    if causal and j > i:
+        return False
+    if window > 0 and (i - j >= window or j - i >= window):
+        return False
+    return True
+
+
+def padded_ext(q, k, v, causal, scale, window, n_global, slopes):
+    """Like padded() with the window / global-row mask and ALiBi slopes (or None)."""
+    B, S, H = len(q), len(q[0]), len(q[0][0])
+    O = [[[None] * H for _ in range(S)] for _ in range(B)]
+    L = [[[None] * S for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            for i in range(S):
+                js = [j for j in range(S) if sees(i, j, causal, window, n_global)]
+                bias = None if slopes is None else [-slopes[h] * abs(i - j) for j in js]
+                O[b][i][h], L[b][h][i] = row(q[b][i][h], [k[b][j][h] for j in js],
+                                             [v[b][j][h] for j in js], scale, bias)
     return O, L
