@@ -55,6 +55,7 @@ def time_workload(cfg, steps: int, warmup: int):
     import numpy as np
     import torch
 
+    import synth
     from scaled_dot_product_08_amd import accounting, binding
 
     inp, (q, k, v), cu = make_device_inputs(cfg)
@@ -62,7 +63,11 @@ def time_workload(cfg, steps: int, warmup: int):
     out = torch.empty_like(q)
     if cu is None:
         lse = torch.empty((cfg.B, cfg.H, cfg.S), dtype=torch.float32, device="cuda")
-        fl = accounting.flops(cfg.B, cfg.H, cfg.S, cfg.D, cfg.causal)
+        if cfg.window or cfg.n_global:
+            fl = accounting.masked_flops(cfg.B, cfg.H, cfg.S, cfg.D, cfg.causal, cfg.window,
+                                         cfg.n_global)
+        else:
+            fl = accounting.flops(cfg.B, cfg.H, cfg.S, cfg.D, cfg.causal)
         nbytes = accounting.min_hbm_bytes(cfg.B, cfg.H, cfg.S, cfg.D, cfg.dtype)
     else:
         lse = torch.empty((cfg.H, cfg.S), dtype=torch.float32, device="cuda")
@@ -70,10 +75,12 @@ def time_workload(cfg, steps: int, warmup: int):
         fl = accounting.varlen_flops(lens, cfg.H, cfg.D, cfg.causal)
         nbytes = accounting.min_hbm_bytes(1, cfg.H, cfg.S, cfg.D, cfg.dtype)
     stream = torch.cuda.current_stream()
+    slopes = torch.from_numpy(synth.alibi_slopes(cfg.H)).cuda() if cfg.alibi else None
 
     def step():
         binding.attn_fwd(q, k, v, out, lse, causal=cfg.causal, scale=scale, cu_seqlens=cu,
-                         stream=stream)
+                         stream=stream, window=cfg.window, n_global=cfg.n_global,
+                         alibi_slopes=slopes)
 
     for _ in range(warmup):
         step()
@@ -156,7 +163,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama", help="key of synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the B4 H12 S2048 D64 side figures")
+    ap.add_argument("--no-extra", action="store_true", help="skip the side figures (B4 H12 S2048 D64, ALiBi, 128K window)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -181,7 +188,7 @@ def main():
 
     also = {}
     if not args.no_extra:
-        for name in ("mha", "mha_causal"):
+        for name in ("mha", "mha_causal", "llama_alibi", "window128k"):
             c2 = synth.CONFIGS[name]
             r2 = time_workload(c2, max(100, args.steps), max(100, args.warmup))
             also[name] = {"workload": c2.describe(), "us_per_call": round(r2["ms"] * 1e3, 2),

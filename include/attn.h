@@ -88,6 +88,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int S, int D, int causal, float scale, int dtype,
              const int32_t* cu_seqlens, void* stream);
 
+/*
+ * attn_fwd_ext -- attn_fwd with the mask and bias variants.
+ *
+ * Same arguments, layouts and errors as attn_fwd, plus:
+ *   window       : sliding-window width in keys, >= 0 (0: no window). Query
+ *                  row i (local index) then sees keys j with i-window < j <= i
+ *                  (causal) or |i-j| < window (non-causal): the sliding-window
+ *                  attention of lnrk.cn/news/11729 §2.5.
+ *   n_global     : >= 0. The first n_global query rows of every sequence see
+ *                  every key of it (the "global tokens" of the same section,
+ *                  whose listing gives the first queries full attention).
+ *   alibi_slopes : NULL, or a DEVICE float32 array of H slopes (4-byte
+ *                  aligned): score_ij gets -slope_h * |i - j| added after
+ *                  scaling -- the ALiBi linear bias named in
+ *                  jianying88.com/news/49672 §5.1.
+ * window < 0 or n_global < 0 -> ATTN_ERR_SHAPE. With window == n_global == 0
+ * and alibi_slopes == NULL the result equals attn_fwd's.
+ */
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int H, int S, int D, int causal, float scale, int dtype,
+                 const int32_t* cu_seqlens, int window, int n_global,
+                 const float* alibi_slopes, void* stream);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* attn_strerror(int status);
 

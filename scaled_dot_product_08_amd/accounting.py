@@ -25,6 +25,35 @@ def varlen_flops(lengths, H: int, D: int, causal: bool) -> float:
     return sum(flops(1, H, int(L), D, causal) for L in lengths)
 
 
+def visible_pairs(L: int, causal: bool, window: int = 0, n_global: int = 0) -> int:
+    """(query, key) pairs of one length-L sequence that the mask lets through.
+
+    Rows below ``n_global`` see all L keys; any other row i sees keys j with
+    j <= i (causal) and i - window < j (window > 0), or |i - j| < window
+    when not causal.
+    """
+    import numpy as np
+    g = min(max(n_global, 0), L)
+    i = np.arange(g, L, dtype=np.int64)
+    if causal:
+        n = i + 1 if window <= 0 else np.minimum(i + 1, window)
+    elif window <= 0:
+        n = np.full(i.shape, L, dtype=np.int64)
+    else:
+        n = np.minimum(L - 1, i + window - 1) - np.maximum(0, i - window + 1) + 1
+    return int(g) * int(L) + int(n.sum())
+
+
+def masked_flops(B: int, H: int, L: int, D: int, causal: bool, window: int = 0,
+                 n_global: int = 0) -> float:
+    """4 * D FLOPs per visible pair (one D-long dot product, one D-long P V update).
+
+    Used for the window / global-row variants, where the visible count is
+    far from S^2/2 and the count itself is the meaningful work.
+    """
+    return 4.0 * D * B * H * visible_pairs(L, causal, window, n_global)
+
+
 def qkv_read_bytes(B: int, H: int, S: int, D: int, dtype: str = "fp16") -> int:
     return 3 * B * H * S * D * ELEM_BYTES[dtype]
 

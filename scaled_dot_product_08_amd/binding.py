@@ -18,7 +18,7 @@ STATUS = {
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN",
 }
-EXPORTS = ("attn_fwd", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -43,6 +43,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_ext.restype = ctypes.c_int
+    lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+         ctypes.c_void_p]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_check_cu_seqlens.restype = ctypes.c_int
@@ -69,6 +73,14 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scal
                                    int(D), int(causal), float(scale), int(dtype), cu_ptr, stream_ptr)
 
 
+def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
+                     cu_ptr, window, n_global, alibi_ptr, stream_ptr) -> int:
+    """Direct call of attn_fwd_ext with integer pointers; returns the status code."""
+    return load_library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
+                                       int(D), int(causal), float(scale), int(dtype), cu_ptr,
+                                       int(window), int(n_global), alibi_ptr, stream_ptr)
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.float16:
@@ -78,6 +90,11 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def torch_float32():
+    import torch
+    return torch.float32
+
+
 def _stream_ptr(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -85,12 +102,14 @@ def _stream_ptr(stream):
 
 
 def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None,
-             cu_seqlens=None, stream=None) -> None:
+             cu_seqlens=None, stream=None, window: int = 0, n_global: int = 0,
+             alibi_slopes=None) -> None:
     """Call attn_fwd on torch device tensors.
 
     Padded: q,k,v,out (B,S,H,D), lse (B,H,S) fp32 or None.
     Packed: q,k,v,out (T,H,D), cu_seqlens int32 (nseq+1,), lse (H,T) or None.
-    ``scale=None`` means 1/sqrt(D) rounded to float32.
+    ``scale=None`` means 1/sqrt(D) rounded to float32. ``window``, ``n_global`` and
+    ``alibi_slopes`` (float32 device tensor of H slopes) call attn_fwd_ext.
     """
     for t in (q, k, v, out):
         if not t.is_contiguous():
@@ -104,15 +123,29 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
         cu_ptr = cu_seqlens.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                      None if lse is None else lse.data_ptr(), B, H, S, D, int(bool(causal)),
-                      scale, _dtype_code(q), cu_ptr, _stream_ptr(stream))
+    lse_ptr = None if lse is None else lse.data_ptr()
+    if window or n_global or alibi_slopes is not None:
+        al = None
+        if alibi_slopes is not None:
+            if (alibi_slopes.dtype != torch_float32() or alibi_slopes.numel() != H
+                    or alibi_slopes.device != q.device or not alibi_slopes.is_contiguous()):
+                raise ValueError("alibi_slopes must be a contiguous float32 tensor of H slopes "
+                                 "on q's device")
+            al = alibi_slopes.data_ptr()
+        st = attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                              B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
+                              window, n_global, al, _stream_ptr(stream))
+    else:
+        st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                          B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
+                          _stream_ptr(stream))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
 
 
 def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
-        with_lse: bool = True, stream=None):
+        with_lse: bool = True, stream=None, window: int = 0, n_global: int = 0,
+        alibi_slopes=None):
     """Allocate O (and LSE) with torch and run attn_fwd. Returns (O, LSE or None)."""
     import torch
     out = torch.empty_like(q)
@@ -124,7 +157,8 @@ def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
         else:
             T, H, _ = q.shape
             lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, out, lse, causal=causal, scale=scale, cu_seqlens=cu_seqlens, stream=stream)
+    attn_fwd(q, k, v, out, lse, causal=causal, scale=scale, cu_seqlens=cu_seqlens, stream=stream,
+             window=window, n_global=n_global, alibi_slopes=alibi_slopes)
     return out, lse
 
 

@@ -92,12 +92,14 @@ int attn_check_cu_seqlens(const int32_t* cu_seqlens, int B, int T, void* stream)
   return ATTN_OK;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
-             int S, int D, int causal, float scale, int dtype, const int32_t* cu_seqlens,
-             void* stream) {
+static int fwd_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                      int H, int S, int D, int causal, float scale, int dtype,
+                      const int32_t* cu_seqlens, int window, int n_global, const float* alibi,
+                      void* stream) {
   long long grid = 0;
   const int st = validate(q, k, v, out, lse, B, H, S, D, scale, dtype, cu_seqlens, &grid);
   if (st != ATTN_OK) return st;
+  if (window < 0 || n_global < 0) return ATTN_ERR_SHAPE;
   const bool packed = cu_seqlens != nullptr;
   if (S == 0 || (packed && B == 0)) return ATTN_OK;
   if (packed && debug_enabled()) {
@@ -126,9 +128,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
     p.c_log2 = log2e;
     p.q_mode = 2;
   }
+  p.window = window;
+  p.n_global = n_global;
+  p.alibi = alibi;
   const hipError_t e = sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
                                           reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+             int S, int D, int causal, float scale, int dtype, const int32_t* cu_seqlens,
+             void* stream) {
+  return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, 0, 0,
+                    nullptr, stream);
+}
+
+int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int H, int S, int D, int causal, float scale, int dtype,
+                 const int32_t* cu_seqlens, int window, int n_global,
+                 const float* alibi_slopes, void* stream) {
+  if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) return ATTN_ERR_ALIGN;
+  return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, window,
+                    n_global, alibi_slopes, stream);
 }
 
 }  // extern "C"

@@ -124,7 +124,9 @@ __device__ __forceinline__ void wait_vmem_all() {
   __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW>
+// EXT: the mask/bias variants (sliding window, global query rows, ALiBi);
+// the plain instances compile none of that code.
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) {
   constexpr int NWAVES = NW;
   constexpr int BM = 32 * NW;                  // query rows per workgroup
@@ -168,7 +170,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   const int bh = grp * HEAD_GROUP + (rem - rank * in_grp);
   const int h = bh % p.H;
   const int b = VARLEN ? 0 : bh / p.H;
-  const int vt = nt - 1 - rank;
+  int vt = nt - 1 - rank;
+  if constexpr (EXT && !VARLEN) {
+    // Tiles holding global rows see every key: they are by far the longest,
+    // so they start first.
+    const int gt = min((p.n_global + BM - 1) / BM, nt);
+    vt = rank < gt ? rank : nt - 1 - (rank - gt);
+  }
   int seq_start = 0, L = p.S, q0;
   if constexpr (VARLEN) {
     // Virtual tile space: sequence s owns tiles [cu[s]/BM + s, ... + ceil(L_s/BM)).
@@ -193,10 +201,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   const uint16_t* vg = p.v + base;
   uint16_t* og = p.o + base + (size_t)q0 * p.H * D;
 
-  const int kv_end = CAUSAL ? min(q0 + BM, L) : L;
-  const int n_kv = (kv_end + BN - 1) / BN;
+  // Key range [kv_lo, kv_hi) any row of this workgroup may see.
+  int kv_lo = 0, kv_hi = CAUSAL ? min(q0 + BM, L) : L;
+  if constexpr (EXT) {
+    if (q0 < p.n_global) {
+      kv_hi = L;                                   // global rows see every key
+    } else if (p.window > 0) {
+      kv_lo = max(0, q0 - p.window + 1);
+      if (!CAUSAL) kv_hi = min(L, q0 + BM - 1 + p.window);
+    }
+  }
+  const int j_lo = kv_lo / BN;
+  const int n_kv = (kv_hi + BN - 1) / BN;          // one past the last tile
   const int wq0 = q0 + wave * 32;        // first query row of this wave
   const int qi = wq0 + li;               // this lane's query row
+  // Mask-variant state of this wave (EXT only).
+  const int win = EXT ? p.window : 0;
+  const int n_glob = EXT ? p.n_global : 0;
+  const bool w_any_glob = EXT && wq0 < n_glob;          // some row of the wave is global
+  const bool w_all_glob = EXT && wq0 + 31 < n_glob;     // every row of the wave is global
+  const float slope2 = (EXT && p.alibi != nullptr) ? p.alibi[h] * 1.4426950408889634f : 0.0f;
+  const bool use_alibi = EXT && p.alibi != nullptr;
   const uint32_t q_rows = (uint32_t)min(L - q0, BM);
 
   // ---- Q^T operand, resident in registers for the whole key loop ----------
@@ -277,8 +302,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   auto compute_tile = [&](int j, const uint8_t* ks) {
     const uint8_t* vs = ks + TILEB;
     const int key0 = j * BN;
-    // A wave whose rows all precede the tile's first key has nothing to do.
-    if (CAUSAL && key0 > wq0 + 31) return;
+    // A wave none of whose rows sees a key of this tile has nothing to do.
+    if constexpr (EXT) {
+      if (!w_any_glob) {
+        if (CAUSAL && key0 > wq0 + 31) return;
+        if (win > 0 && key0 + BN - 1 <= wq0 - win) return;
+        if (win > 0 && !CAUSAL && key0 >= wq0 + 31 + win) return;
+      }
+    } else {
+      if (CAUSAL && key0 > wq0 + 31) return;
+    }
 
     // S^T = K Q^T for two 32-key blocks. The two accumulation chains
     // alternate (a chain's next MFMA waits for its previous result) and the
@@ -314,8 +347,50 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 
     // Mask keys past the sequence end and, under causality, keys after the
     // query (only tiles that reach those positions pay for it).
-    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
-    if (need_mask) {
+    bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
+    if constexpr (EXT) {
+      // every row of the wave sees every key of the tile, or not
+      bool all_vis = key0 + BN <= L;
+      if (!w_all_glob) {
+        if (CAUSAL && key0 + BN - 1 > wq0) all_vis = false;
+        if (win > 0 && key0 <= wq0 + 31 - win) all_vis = false;
+        if (win > 0 && !CAUSAL && key0 + BN - 1 >= wq0 + win) all_vis = false;
+        if (w_any_glob && !all_vis) all_vis = false;
+      }
+      need_mask = !all_vis;
+    }
+    if constexpr (EXT) {
+      const bool glob_row = qi < n_glob;
+      if (use_alibi) {
+        // Work in the log2-scaled domain: t = s * c - slope * |i - j|.
+        // slope * (j - i) = slope * (key0 + 4 hh - i) + slope * (offset of
+        // the register), and -|x| = min(x, -x).
+        const float bl = slope2 * (float)(key0 + hh * 4 - qi);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float u = fmaf(slope2, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), bl);
+            s[kb][r] = fmaf(s[kb][r], c_log2, fminf(u, -u));
+          }
+        }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+            bool ok = key < L;
+            if (!glob_row) {
+              if (CAUSAL) ok = ok && key <= qi;
+              if (win > 0) ok = ok && key > qi - win && (CAUSAL || key < qi + win);
+            }
+            s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          }
+        }
+      }
+    } else if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -334,7 +409,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     mx = fmaxf(mx, wave_xor32(mx));
-    const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
+    // With ALiBi the scores are already log2-scaled.
+    const bool prescaled = EXT && use_alibi;
+    const float mx2 = prescaled ? mx : ((mx == -INFINITY) ? -INFINITY : mx * c_log2);
 
     // Lazy refresh of the running maximum.
     const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
@@ -354,12 +431,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     // error below 2.5e-4 and sums the rounded pairs with one dot2.
     uint32_t pk[2][8];
     float tile_l = 0.0f;
+    // A row that has seen no visible key yet keeps m = -inf (its scores here
+    // are all -inf too): subtract 0 instead, which gives exp2(-inf) = 0.
+    const float m_sub = (EXT && m_run == -INFINITY) ? 0.0f : m_run;
+    const float c_mul = prescaled ? 1.0f : c_log2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_log2, -m_run));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_log2, -m_run));
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_mul, -m_sub));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_mul, -m_sub));
         pk[kb][t] = pack2<BF16>(e0, e1);
         if constexpr (BF16) {
           tile_l += e0 + e1;
@@ -390,11 +471,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   };
 
   // ---- main loop: two-stage LDS ring, unrolled by two ----------------------
-  issue_tile(0, 0);
+  issue_tile(j_lo, 0);
   wait_vmem_all();
   __syncthreads();
 #pragma unroll 1
-  for (int j = 0; j < n_kv; j += 2) {
+  for (int j = j_lo; j < n_kv; j += 2) {
     if (j + 1 < n_kv) issue_tile(j + 1, 1);
     compute_tile(j, smem0);
     wait_vmem_all();
@@ -452,21 +533,25 @@ static int choose_waves(const FwdParams& p, bool varlen) {
 int max_query_tile_rows() { return 256; }
 int min_query_tile_rows() { return 128; }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT>
 static hipError_t launch_one(FwdParams p, hipStream_t stream) {
   constexpr long long BM = 32 * NW;
   const long long tiles = VARLEN ? (long long)p.S / BM + p.B : ((long long)p.S + BM - 1) / BM;
   p.n_qtiles = (int)tiles;
   const long long grid = tiles * (VARLEN ? p.H : (long long)p.B * p.H);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW, EXT>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 static hipError_t launch_nw(const FwdParams& p, hipStream_t stream) {
-  return choose_waves(p, VARLEN) == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8>(p, stream)
-                                      : launch_one<D, BF16, CAUSAL, VARLEN, 4>(p, stream);
+  // The mask/bias variants run with 4-wave workgroups only.
+  if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
+    return launch_one<D, BF16, CAUSAL, VARLEN, 4, true>(p, stream);
+  }
+  return choose_waves(p, VARLEN) == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, stream)
+                                      : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, stream);
 }
 
 template <int D, bool BF16>

@@ -18,6 +18,9 @@ struct FwdParams {
   int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed); set at launch
   float c_log2;             // |scale| * log2(e), or log2(e) when scale == 0
   int q_mode;               // 0: scale > 0, 1: scale < 0 (use -Q), 2: scale == 0 (Q := 0)
+  int window;               // sliding-window width in keys (0: none)
+  int n_global;             // leading query rows of each sequence that see every key
+  const float* alibi;       // per-head ALiBi slopes (device), or null
 };
 
 // Largest / smallest query tile (rows per workgroup) the launcher may pick.

@@ -138,6 +138,9 @@ class Config:
     seg_hi: int = 0
     sample_rows: int = 0
     extra: dict = field(default_factory=dict)
+    window: int = 0             # sliding-window width (0: none)
+    n_global: int = 0           # leading query rows that see every key
+    alibi: bool = False         # per-head linear distance bias (slopes from alibi_slopes)
 
     @property
     def seed(self) -> int:
@@ -148,7 +151,14 @@ class Config:
         if self.varlen:
             return (f"varlen T={self.S} H={self.H} D={self.D} {self.dtype} {c} "
                     f"segments U[{self.seg_lo},{self.seg_hi}]")
-        return f"B={self.B} H={self.H} S={self.S} D={self.D} {self.dtype} {c}"
+        d = f"B={self.B} H={self.H} S={self.S} D={self.D} {self.dtype} {c}"
+        if self.window:
+            d += f" window={self.window}"
+        if self.n_global:
+            d += f" global={self.n_global}"
+        if self.alibi:
+            d += " alibi"
+        return d
 
 
 CONFIGS = {
@@ -159,7 +169,18 @@ CONFIGS = {
     "long": Config(4, "long", 1, 32, 65536, 64, "fp16", True, sample_rows=256),
     "varlen": Config(5, "varlen", 1, 32, 65536, 128, "bf16", True, varlen=True,
                      seg_lo=128, seg_hi=8192),
+    # mask/bias variants: a 128K-token context with a 4096-key causal window
+    # and 64 global query rows; the LLaMA-shaped layer with ALiBi slopes
+    "window128k": Config(6, "window128k", 1, 32, 131072, 128, "bf16", True, window=4096,
+                         n_global=64),
+    "llama_alibi": Config(3, "llama_alibi", 4, 32, 4096, 128, "bf16", True, mult=0.5,
+                          alibi=True),
 }
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """Per-head ALiBi slopes, the geometric schedule 2^(-8(h+1)/H), as float32."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
 
 
 @dataclass

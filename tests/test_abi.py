@@ -67,3 +67,24 @@ def test_argument_errors(kw, code):
 def test_empty_problems_are_noops(kw):
     # Returns before any HIP call: nothing to compute.
     assert call(**kw) == 0
+
+
+def call_ext(window=0, n_global=0, alibi=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=2, S=128, D=64, causal=0, scale=0.125,
+             dtype=binding.ATTN_DTYPE_FP16, cu=None)
+    a.update(kw)
+    return binding.attn_fwd_ext_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                                    a["D"], a["causal"], a["scale"], a["dtype"], a["cu"], window,
+                                    n_global, alibi, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), -2), (dict(n_global=-5), -2), (dict(alibi=P + 2), -8),
+    (dict(D=80, window=8), -5), (dict(q=None, window=8), -1), (dict(scale=float("nan"), n_global=2), -4),
+])
+def test_ext_argument_errors(kw, code):
+    assert call_ext(**kw) == code
+
+
+def test_ext_empty_problem_is_noop():
+    assert call_ext(window=16, S=0) == 0

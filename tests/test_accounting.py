@@ -51,3 +51,25 @@ def test_causal_halves_and_varlen_sums():
 def test_config_table_bytes():
     c = synth.CONFIGS["llama"]
     assert acc.min_hbm_bytes(c.B, c.H, c.S, c.D, c.dtype) == pytest.approx(539.0e6, rel=2e-3)
+
+
+@pytest.mark.parametrize("L", [1, 7, 64, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window,n_global", [(0, 0), (1, 0), (5, 0), (64, 3), (300, 0), (0, 9),
+                                             (16, 250)])
+def test_visible_pairs_counts_the_mask(L, causal, window, n_global):
+    """The closed form equals the number of pairs the oracle's mask lets through."""
+    import numpy as np
+    from oracle.attention import visible_mask
+    m = visible_mask(np.arange(L), L, causal, window, n_global)
+    assert acc.visible_pairs(L, causal, window, n_global) == int(m.sum())
+
+
+def test_masked_flops_plain_cases():
+    # no mask: S^2 pairs; causal without window: S(S+1)/2 pairs
+    assert acc.masked_flops(2, 3, 100, 64, False) == acc.flops(2, 3, 100, 64, False)
+    assert acc.masked_flops(1, 1, 100, 64, True) == 4.0 * 64 * 5050
+    # window 4096 over 128K keys with 64 global rows
+    L, W, G = 131072, 4096, 64
+    want = G * L + sum(min(i + 1, W) for i in range(G, L))
+    assert acc.visible_pairs(L, True, W, G) == want

@@ -1,0 +1,102 @@
+"""GPU parity of the mask/bias variants (attn_fwd_ext): sliding window, global rows, ALiBi."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import TOL_LSE, TOL_O, max_abs, say, scale_of, to_dev, to_f64
+from oracle import attention, attention_rows
+from scaled_dot_product_08_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+# Narrow windows and steep ALiBi slopes concentrate a row's weight on a few
+# keys, so |O| approaches |V| (up to ~4 for N(0,1) inputs). The 16-bit output
+# then carries a rounding error of up to 2^-(p+1)|O| from its own store and
+# as much again from the rounded probabilities (p = 8 significant bits for
+# bf16, 11 for fp16): the bound is the absolute tolerance plus 2^-p |O_ref|.
+REL_O = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
+
+
+def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=None):
+    q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
+    sl = None if slopes is None else torch.from_numpy(slopes).cuda()
+    cud = None if cu is None else torch.from_numpy(cu).cuda()
+    o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cud, window=window,
+                         n_global=n_global, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    f = [synth.bits_to_f64(x, dtype) for x in (qb, kb, vb)]
+    oref, lref = attention(*f, causal=causal, scale=scale, cu_seqlens=cu, window=window,
+                           n_global=n_global, alibi_slopes=slopes)
+    og = to_f64(o)
+    eo, el = max_abs(og, oref), max_abs(lse.cpu().numpy(), lref)
+    excess = float((np.abs(og - oref) - (TOL_O[dtype] + REL_O[dtype] * np.abs(oref))).max())
+    say(f"    max|dO|={eo:.3e} max|dLSE|={el:.3e} worst excess over bound={excess:.3e}")
+    assert excess <= 0.0, (eo, excess)
+    assert el <= TOL_LSE, el
+
+
+VARIANTS = [(64, 0, False), (100, 0, False), (1, 0, False), (128, 5, False), (0, 70, False),
+            (0, 0, True), (200, 64, True), (33, 1, True)]
+
+
+@pytest.mark.parametrize("window,n_global,alibi", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D,dtype", [(64, "fp16"), (128, "bf16"), (64, "bf16"), (128, "fp16")])
+def test_ext_padded(window, n_global, alibi, causal, D, dtype):
+    B, S, H = 2, 333, 3
+    say(f"ext padded S={S} D={D} {dtype} causal={causal} window={window} global={n_global} alibi={alibi}")
+    qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 4000 + window + n_global)
+    run_check(qb, kb, vb, dtype, causal, scale_of(D), window, n_global,
+              synth.alibi_slopes(H) if alibi else None)
+
+
+@pytest.mark.parametrize("window,n_global,alibi", [(64, 0, False), (50, 10, True), (0, 0, True)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ext_packed(window, n_global, alibi, causal):
+    lens = [1, 3, 0, 130, 257, 64, 200, 513]
+    cu = synth.cu_seqlens_of(lens)
+    T, H, D = int(cu[-1]), 2, 128
+    say(f"ext packed causal={causal} window={window} global={n_global} alibi={alibi}")
+    qb, kb, vb = synth.normal_qkv((T, H, D), "bf16", 4100)
+    run_check(qb, kb, vb, "bf16", causal, scale_of(D), window, n_global,
+              synth.alibi_slopes(H) if alibi else None, cu=cu)
+
+
+def test_ext_zero_slopes_match_plain():
+    qb, kb, vb = synth.normal_qkv((1, 300, 2, 64), "fp16", 4200)
+    q, k, v = (to_dev(x, "fp16") for x in (qb, kb, vb))
+    o0, l0 = binding.fwd(q, k, v, causal=True)
+    o1, l1 = binding.fwd(q, k, v, causal=True, alibi_slopes=torch.zeros(2, device="cuda"))
+    torch.cuda.synchronize()
+    assert (o0.float() - o1.float()).abs().max().item() <= 2e-3
+    assert (l0 - l1).abs().max().item() <= 1e-5
+
+
+def test_window_one_returns_v_bitwise():
+    qb, kb, vb = synth.normal_qkv((2, 150, 2, 128), "bf16", 4300)
+    q, k, v = (to_dev(x, "bf16") for x in (qb, kb, vb))
+    o, _ = binding.fwd(q, k, v, causal=True, window=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+
+
+def test_long_window_global_sampled():
+    """The pages' long-context scheme: window 4096 plus 64 global query rows, B1 H32 S65536 D128."""
+    S, H, D, W, G = 65536, 32, 128, 4096, 64
+    say(f"window workload S={S} H={H} D={D} window={W} global={G}")
+    qb, kb, vb = synth.normal_qkv((1, S, H, D), "bf16", 4400)
+    q, k, v = (to_dev(x, "bf16") for x in (qb, kb, vb))
+    o, lse = binding.fwd(q, k, v, causal=True, window=W, n_global=G)
+    torch.cuda.synchronize()
+    rows = synth.sampled_rows(S, 48, 4401, must=(0, 1, 63, 64, 65, 4095, 4096, 4097))
+    heads = [0, 17, 31]
+    f = [synth.bits_to_f64(x[0][:, heads], "bf16") for x in (qb, kb, vb)]
+    oref, lref = attention_rows(*f, rows, causal=True, scale=scale_of(D), window=W, n_global=G)
+    o, lse = o.cpu(), lse.cpu()
+    og = o[0][rows][:, heads].float().numpy().astype(np.float64)
+    eo = max_abs(og, oref)
+    el = max_abs(lse[0][heads][:, rows].numpy(), lref)
+    excess = float((np.abs(og - oref) - (TOL_O["bf16"] + REL_O["bf16"] * np.abs(oref))).max())
+    say(f"    sampled max|dO|={eo:.3e} max|dLSE|={el:.3e} excess={excess:.3e}")
+    assert excess <= 0.0 and el <= TOL_LSE
