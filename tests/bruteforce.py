@@ -81,3 +81,24 @@ def padded_ext(q, k, v, causal, scale, window, n_global, slopes):
                 O[b][i][h], L[b][h][i] = row(q[b][i][h], [k[b][j][h] for j in js],
                                              [v[b][j][h] for j in js], scale, bias)
     return O, L
+
+
+def decode(q, kc, vc, lens, causal, scale):
+    """KV-cache decode: q [B][Sq][H][D], caches [B][H][S_max][D], valid lengths per sequence.
+    Query row i sits at position L - Sq + i; under causality it sees keys up to there.
+    Returns (O [B][Sq][H][D], LSE [B][H][Sq]); rows with no visible key give zeros and -inf."""
+    B, Sq, H = len(q), len(q[0]), len(q[0][0])
+    Dv = len(vc[0][0][0])
+    O = [[[None] * H for _ in range(Sq)] for _ in range(B)]
+    L_ = [[[None] * Sq for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        L = lens[b]
+        for h in range(H):
+            for i in range(Sq):
+                js = [j for j in range(L) if not causal or j <= L - Sq + i]
+                if not js:
+                    O[b][i][h], L_[b][h][i] = [0.0] * Dv, -math.inf
+                    continue
+                O[b][i][h], L_[b][h][i] = row(q[b][i][h], [kc[b][h][j] for j in js],
+                                              [vc[b][h][j] for j in js], scale)
+    return O, L_
