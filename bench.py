@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (B4 H12 S2048 D64 fp16; S4096 D128 bf16)"
 PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak bandwidth
 KERNEL_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_fwd_kernel.hip",
                   "scaled_dot_product_08_amd/csrc/attn_kernel.h"]
 
@@ -95,6 +96,49 @@ def time_workload(cfg, steps: int, warmup: int):
     ms = t0.elapsed_time(t1) / steps
     return {"ms": ms, "flops": fl, "bytes": nbytes, "tflops": fl / (ms * 1e-3) / 1e12,
             "sha256": inp.sha256}
+
+
+def time_decode(cfg, steps: int, warmup: int):
+    """KV-cache decode step: mean over ``steps`` launches, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import synth
+    from scaled_dot_product_08_amd import accounting, binding
+
+    dt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    inp = synth.make_decode_inputs(cfg)
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(dt).cuda() for x in (inp.q, inp.k, inp.v))
+    sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
+    lens = [cfg.S_max] * cfg.B if inp.seqlens is None else inp.seqlens.tolist()
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.Sq), dtype=torch.float32, device="cuda")
+    ws_bytes = binding.decode_workspace_size(cfg.B, cfg.H, cfg.Sq, cfg.S_max, cfg.D, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1.0 / math.sqrt(cfg.D)))
+    stream = torch.cuda.current_stream()
+
+    def step():
+        binding.attn_decode(q, k, v, out, lse, seqlens_k=sl, causal=cfg.causal, scale=scale,
+                            workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    nbytes = accounting.decode_bytes(cfg.B, cfg.H, cfg.Sq, cfg.D, lens, cfg.dtype)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": cfg.describe(), "us_per_call": round(ms * 1e3, 2),
+            "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "tflops": round(accounting.decode_flops(cfg.H, cfg.Sq, cfg.D, lens) / (ms * 1e-3) / 1e12, 2)}
 
 
 def read_traffic(workload: str):
@@ -195,6 +239,13 @@ def main():
                           "tflops": round(r2["tflops"], 1),
                           "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4)}
             log(f"  {name}: {r2['ms'] * 1e3:.1f} us, {r2['tflops']:.1f} TFLOP/s")
+
+    if not args.no_extra:
+        for name, c3 in synth.DECODE_CONFIGS.items():
+            r3 = time_decode(c3, max(100, args.steps), max(50, args.warmup))
+            also[name] = r3
+            log(f"  {name}: {r3['us_per_call']:.1f} us, {r3['GB_per_s']:.0f} GB/s "
+                f"({100 * r3['frac_of_hbm_peak']:.1f} % of HBM peak)")
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4

@@ -18,6 +18,7 @@
 #ifndef SDPA08_ATTN_H
 #define SDPA08_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -40,7 +41,8 @@ enum {
   ATTN_ERR_UNSUPPORTED = -5, /* head dimension D is not 64 or 128 */
   ATTN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
   ATTN_ERR_SEQLENS = -7,     /* cu_seqlens failed validation (debug check) */
-  ATTN_ERR_ALIGN = -8        /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_ALIGN = -8,       /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = -9    /* attn_decode: workspace NULL or too small */
 };
 
 /*
@@ -110,6 +112,46 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                  int B, int H, int S, int D, int causal, float scale, int dtype,
                  const int32_t* cu_seqlens, int window, int n_global,
                  const float* alibi_slopes, void* stream);
+
+/*
+ * attn_decode -- attention of a few new query rows against a KV cache.
+ *
+ * The decode step of autoregressive generation: the cache holds keys and
+ * values of earlier tokens in the [batch, heads, seq_len, head_dim] layout of
+ * lnrk.cn/news/11729 §2.2 (which notes that it grows by one row per
+ * generated token); the new rows attend to it with the definition of
+ * mlqm.cn/news/343191 chapter 1.
+ *   q         : contiguous (B, Sq, H, D) array of `dtype` (Sq new rows per sequence).
+ *   k_cache,
+ *   v_cache   : contiguous (B, H, S_max, D) arrays of `dtype`.
+ *   seqlens_k : int32 DEVICE array of B valid cache lengths, or NULL (all
+ *               S_max). Values are clamped to [0, S_max]; rows past a
+ *               sequence's length are never read.
+ *   out       : contiguous (B, Sq, H, D) array of `dtype`.
+ *   lse       : contiguous (B, H, Sq) float32 (natural log), or NULL.
+ * Query row i of sequence b sits at position L_b - Sq + i. Without causality
+ * it sees all L_b valid rows; with causal != 0 it sees rows j <= L_b - Sq + i.
+ * A row that sees none (L_b == 0, or L_b < Sq under causality) gets out = 0
+ * and lse = -inf.
+ *   D : 64 or 128.  scale : any finite float.  B, Sq, S_max >= 0, H >= 1;
+ *   S_max * D * 2 bytes must stay below 4 GiB - 1 MiB.
+ *   num_splits : 0 picks the split count from the shapes; n > 0 asks for at
+ *               most n splits of the cache rows per query row (capped at 256).
+ *   workspace  : DEVICE memory of at least attn_decode_workspace_size(...)
+ *               bytes for the same B, H, Sq, S_max, D and num_splits,
+ *               16-byte aligned, owned by the caller and used as scratch
+ *               (partial results of the splits) until the stream reaches the
+ *               end of the call. May be NULL when that size is 0 (one split).
+ * Two kernels run on `stream` when there is more than one split (per-split
+ * partial results, then their log-sum-exp merge), one otherwise. Errors as
+ * attn_fwd, plus ATTN_ERR_WORKSPACE.
+ */
+size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int num_splits);
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* attn_strerror(int status);

@@ -74,3 +74,21 @@ def logits_bytes(S: int, elem: int = 2) -> int:
 
 def arithmetic_intensity(fl: float, nbytes: float) -> float:
     return fl / nbytes
+
+
+def decode_bytes(B: int, H: int, Sq: int, D: int, lengths, dtype: str,
+                 with_lse: bool = True) -> int:
+    """Minimum HBM traffic of one decode step: the valid K and V cache rows
+    read once, Q read once, O written once (+ fp32 LSE written once)."""
+    e = ELEM_BYTES[dtype]
+    rows = sum(int(L) for L in lengths)
+    n = 2 * rows * H * D * e + 2 * B * Sq * H * D * e
+    if with_lse:
+        n += 4 * B * H * Sq
+    return n
+
+
+def decode_flops(H: int, Sq: int, D: int, lengths) -> float:
+    """4 * D FLOPs per (query row, cache row) pair (non-causal count)."""
+    return 4.0 * D * H * Sq * sum(int(L) for L in lengths)
+

@@ -16,9 +16,10 @@ ATTN_DTYPE_BF16 = 1
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
-    -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN",
+    -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_decode", "attn_decode_workspace_size", "attn_strerror",
+           "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -47,6 +48,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
          ctypes.c_void_p]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+         ctypes.c_void_p]
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_check_cu_seqlens.restype = ctypes.c_int
@@ -79,6 +86,20 @@ def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, 
     return load_library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
                                        int(D), int(causal), float(scale), int(dtype), cu_ptr,
                                        int(window), int(n_global), alibi_ptr, stream_ptr)
+
+
+def attn_decode_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq, S_max, D, causal,
+                    scale, dtype, num_splits, ws_ptr, ws_bytes, stream_ptr) -> int:
+    """Direct call of attn_decode with integer pointers; returns the status code."""
+    return load_library().attn_decode(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, int(B),
+                                      int(H), int(Sq), int(S_max), int(D), int(causal),
+                                      float(scale), int(dtype), int(num_splits), ws_ptr,
+                                      int(ws_bytes), stream_ptr)
+
+
+def decode_workspace_size(B, H, Sq, S_max, D, num_splits=0) -> int:
+    return int(load_library().attn_decode_workspace_size(int(B), int(H), int(Sq), int(S_max),
+                                                          int(D), int(num_splits)))
 
 
 def _dtype_code(t) -> int:
@@ -165,3 +186,51 @@ def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
 def check_cu_seqlens(cu_seqlens, T: int, stream=None) -> int:
     return load_library().attn_check_cu_seqlens(cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
                                                 int(T), _stream_ptr(stream))
+
+
+def attn_decode(q, k_cache, v_cache, out, lse=None, *, seqlens_k=None, causal: bool = False,
+                scale: float | None = None, num_splits: int = 0, workspace=None,
+                stream=None) -> None:
+    """Call attn_decode on torch device tensors.
+
+    q, out (B, Sq, H, D); k_cache, v_cache (B, H, S_max, D); seqlens_k int32 (B,) or None;
+    lse (B, H, Sq) fp32 or None; workspace a device tensor of at least
+    decode_workspace_size(...) bytes (allocated here with torch when None).
+    """
+    import torch
+    for t in (q, k_cache, v_cache, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    B, Sq, H, D = q.shape
+    S_max = k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, H, S_max, D) or tuple(v_cache.shape) != (B, H, S_max, D):
+        raise ValueError("k_cache and v_cache must be (B, H, S_max, D)")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B
+                                  or seqlens_k.device != q.device):
+        raise ValueError("seqlens_k must be an int32 tensor of B lengths on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_size(B, H, Sq, S_max, D, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = attn_decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                         None if seqlens_k is None else seqlens_k.data_ptr(), out.data_ptr(),
+                         None if lse is None else lse.data_ptr(), B, H, Sq, S_max, D,
+                         int(bool(causal)), scale, _dtype_code(q), num_splits, ws_ptr, ws_bytes,
+                         _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+
+
+def decode(q, k_cache, v_cache, *, seqlens_k=None, causal: bool = False, scale: float | None = None,
+           num_splits: int = 0, with_lse: bool = True, stream=None):
+    """Allocate O (and LSE) with torch and run attn_decode. Returns (O, LSE or None)."""
+    import torch
+    B, Sq, H, _ = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if with_lse else None
+    attn_decode(q, k_cache, v_cache, out, lse, seqlens_k=seqlens_k, causal=causal, scale=scale,
+                num_splits=num_splits, stream=stream)
+    return out, lse

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/attn.h"
+#include "attn_decode.h"
 #include "attn_kernel.h"
 
 namespace {
@@ -54,6 +55,33 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
   return ATTN_OK;
 }
 
+// Validation of attn_decode's arguments; no HIP call. Fills the split plan.
+int validate_decode(const void* q, const void* k, const void* v, void* out, const float* lse,
+                    int B, int H, int Sq, int S_max, int D, float scale, int dtype,
+                    int num_splits, sdpa08::DecodePlan* plan) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B < 0 || H < 1 || H > 65535 || Sq < 0 || S_max < 0 || num_splits < 0) return ATTN_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return ATTN_ERR_ALIGN;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_ALIGN;
+  // Byte offsets inside one (batch, head) cache slice are 32-bit, with room
+  // for the last partial step past the end.
+  if ((long long)S_max * D * 2 + (1LL << 20) > (long long)UINT32_MAX) return ATTN_ERR_SHAPE;
+  const long double elems = (long double)B * H * ((long double)S_max + Sq) * D;
+  if (elems > (long double)LLONG_MAX / 2) return ATTN_ERR_SHAPE;
+  *plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits);
+  const long long rows = (long long)B * H * Sq;
+  if (rows * plan->n_splits > INT_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+size_t decode_workspace_bytes(long long rows, const sdpa08::DecodePlan& plan, int D) {
+  if (plan.n_splits <= 1) return 0;
+  return (size_t)rows * plan.n_splits * (size_t)(D + 1) * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,6 +99,7 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_LAUNCH: return "HIP runtime error at launch";
     case ATTN_ERR_SEQLENS: return "cu_seqlens is not a valid prefix-offset array";
     case ATTN_ERR_ALIGN: return "tensor pointer misaligned (q/k/v/out need 16 bytes, lse 4)";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_size";
     default: return "unknown status";
   }
 }
@@ -150,6 +179,48 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
   if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) return ATTN_ERR_ALIGN;
   return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, window,
                     n_global, alibi_slopes, stream);
+}
+
+size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int num_splits) {
+  if (B < 0 || H < 1 || Sq < 0 || S_max < 0 || num_splits < 0 || (D != 64 && D != 128)) return 0;
+  const sdpa08::DecodePlan plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits);
+  return decode_workspace_bytes((long long)B * H * Sq, plan, D);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa08::DecodePlan plan{1, 0};
+  const int st = validate_decode(q, k_cache, v_cache, out, lse, B, H, Sq, S_max, D, scale, dtype,
+                                 num_splits, &plan);
+  if (st != ATTN_OK) return st;
+  if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
+  const long long rows = (long long)B * H * Sq;
+  const size_t need = decode_workspace_bytes(rows, plan, D);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  if (rows == 0) return ATTN_OK;
+  sdpa08::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k_cache);
+  p.v = static_cast<const uint16_t*>(v_cache);
+  p.seqlens = seqlens_k;
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_lse = need > 0 ? p.part_o + (size_t)rows * plan.n_splits * D : nullptr;
+  p.B = B;
+  p.H = H;
+  p.Sq = Sq;
+  p.S_max = S_max;
+  p.n_splits = plan.n_splits;
+  p.chunk = plan.chunk;
+  p.c_log2 = scale * 1.4426950408889634f;
+  p.causal = causal != 0;
+  const hipError_t e = sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16,
+                                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

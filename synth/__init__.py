@@ -212,3 +212,74 @@ def make_inputs(cfg: Config, *, S: int | None = None, B: int | None = None,
         return Inputs(q, k, v, cfg.dtype, "thd", cu, sha256_of(q, k, v, cu))
     q, k, v = normal_qkv((B, S, H, cfg.D), cfg.dtype, cfg.seed, cfg.mult)
     return Inputs(q, k, v, cfg.dtype, "bshd", None, sha256_of(q, k, v))
+
+
+# ---- KV-cache decode workloads ---------------------------------------------
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    """One decode step: Sq new rows per sequence against a (B, H, S_max, D) cache."""
+    index: int
+    name: str
+    B: int
+    H: int
+    Sq: int
+    S_max: int
+    D: int
+    dtype: str
+    causal: bool
+    len_lo: int = 0          # 0: every cache is full (S_max rows)
+    len_hi: int = 0
+
+    @property
+    def seed(self) -> int:
+        return config_seed(self.index)
+
+    def describe(self) -> str:
+        c = " causal" if self.causal else ""
+        lens = (f" lengths U[{self.len_lo},{self.len_hi}]" if self.len_lo else " full caches")
+        return (f"decode B={self.B} H={self.H} Sq={self.Sq} S_max={self.S_max} D={self.D} "
+                f"{self.dtype}{c}{lens}")
+
+
+DECODE_CONFIGS = {
+    # one new token per sequence against a 64K-token cache (LLaMA-shaped heads)
+    "decode64k": DecodeConfig(7, "decode64k", 4, 32, 1, 65536, 128, "bf16", False),
+    # a serving batch: 32 sequences with cache lengths spread over [1, 8192]
+    "decode_batch": DecodeConfig(8, "decode_batch", 32, 32, 1, 8192, 128, "bf16", False,
+                                 len_lo=1, len_hi=8192),
+}
+
+
+@dataclass
+class DecodeInputs:
+    q: np.ndarray                 # (B, Sq, H, D) bits
+    k: np.ndarray                 # (B, H, S_max, D) bits
+    v: np.ndarray
+    seqlens: np.ndarray | None    # int32 (B,) or None
+    dtype: str
+    sha256: str
+
+
+def decode_lengths(B: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Cache lengths drawn uniformly in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def decode_inputs(B: int, Sq: int, H: int, S_max: int, D: int, dtype: str, seed: int,
+                  lens=None) -> DecodeInputs:
+    """Q then K then V, i.i.d. N(0,1), rounded to the element type."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = to_bits(rng.standard_normal(size=(B, Sq, H, D), dtype=np.float32), dtype)
+    k = to_bits(rng.standard_normal(size=(B, H, S_max, D), dtype=np.float32), dtype)
+    v = to_bits(rng.standard_normal(size=(B, H, S_max, D), dtype=np.float32), dtype)
+    sl = None if lens is None else np.asarray(lens, dtype=np.int32)
+    extra = () if sl is None else (sl,)
+    return DecodeInputs(q, k, v, sl, dtype, sha256_of(q, k, v, *extra))
+
+
+def make_decode_inputs(cfg: DecodeConfig) -> DecodeInputs:
+    lens = (decode_lengths(cfg.B, cfg.len_lo, cfg.len_hi, cfg.seed + 1) if cfg.len_lo else None)
+    return decode_inputs(cfg.B, cfg.Sq, cfg.H, cfg.S_max, cfg.D, cfg.dtype, cfg.seed, lens)
+

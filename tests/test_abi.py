@@ -88,3 +88,41 @@ def test_ext_argument_errors(kw, code):
 
 def test_ext_empty_problem_is_noop():
     assert call_ext(window=16, S=0) == 0
+
+
+def call_dec(**kw):
+    a = dict(q=P, k=P, v=P, sl=None, o=P, lse=None, B=2, H=4, Sq=1, S_max=4096, D=128, causal=0,
+             scale=0.1, dtype=binding.ATTN_DTYPE_BF16, ns=0, ws=None, wsb=0)
+    a.update(kw)
+    return binding.attn_decode_raw(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"], a["B"],
+                                   a["H"], a["Sq"], a["S_max"], a["D"], a["causal"], a["scale"],
+                                   a["dtype"], a["ns"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(dtype=5), -3), (dict(D=80), -5), (dict(scale=float("inf")), -4),
+    (dict(H=0), -2), (dict(B=-1), -2), (dict(Sq=-1), -2), (dict(S_max=-1), -2), (dict(ns=-2), -2),
+    (dict(S_max=1 << 24), -2),
+    (dict(q=P + 4), -8), (dict(lse=P + 1), -8), (dict(ns=1, sl=P + 2), -8),
+    (dict(ns=4), -9), (dict(ns=4, ws=P, wsb=100), -9),
+])
+def test_decode_argument_errors(kw, code):
+    assert call_dec(**kw) == code
+
+
+def test_decode_workspace_size_rules(lib):
+    ws = binding.decode_workspace_size
+    assert ws(2, 4, 1, 4096, 128, 1) == 0                    # one split: no workspace
+    n = ws(2, 4, 1, 4096, 128, 4)
+    assert n == 2 * 4 * 1 * 4 * 129 * 4                      # rows x splits x (D + 1) floats
+    assert ws(4, 32, 1, 65536, 128, 0) > 0                   # automatic split count
+    assert ws(4, 32, 1, 65536, 128, 100000) <= 4 * 32 * 256 * 129 * 4   # capped at 256 splits
+    assert ws(1, 1, 1, 0, 64, 0) == 0
+    # a too-small workspace is refused before anything is enqueued
+    assert call_dec(ns=4, ws=P, wsb=n // 2 - 1, B=2, H=4) == -9
+
+
+def test_decode_empty_problem_is_noop():
+    assert call_dec(B=0) == 0
+    assert call_dec(Sq=0) == 0

@@ -1,0 +1,126 @@
+"""GPU parity of attn_decode (KV-cache attention, split-KV) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import TOL_LSE, TOL_O, max_abs, say, scale_of, to_dev, to_f64
+from oracle import decode_attention
+from scaled_dot_product_08_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+def run(inp, causal, scale, num_splits=0, with_lse=True):
+    q, k, v = (to_dev(x, inp.dtype) for x in (inp.q, inp.k, inp.v))
+    sl = None if inp.seqlens is None else torch.from_numpy(inp.seqlens).cuda()
+    o, lse = binding.decode(q, k, v, seqlens_k=sl, causal=causal, scale=scale,
+                            num_splits=num_splits, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(inp, causal, scale, num_splits=0):
+    o, lse = run(inp, causal, scale, num_splits)
+    f = [synth.bits_to_f64(x, inp.dtype) for x in (inp.q, inp.k, inp.v)]
+    oref, lref = decode_attention(*f, causal=causal, scale=scale, seqlens_k=inp.seqlens)
+    og, lg = to_f64(o), lse.cpu().numpy().astype(np.float64)
+    # rows that see no key: exactly zero and -inf
+    empty = np.isneginf(lref)
+    assert np.array_equal(np.isneginf(lg), empty)
+    eo = max_abs(og, oref)
+    el = max_abs(lg[~empty], lref[~empty])
+    say(f"    max|dO|={eo:.3e} max|dLSE|={el:.3e} empty rows={int(empty.sum())}")
+    assert eo <= TOL_O[inp.dtype], eo
+    assert el <= TOL_LSE, el
+    return o, lse
+
+
+CASES = [
+    # B, Sq, H, S_max, D, lengths (None = full)
+    (2, 1, 3, 1000, 128, None),
+    (3, 1, 2, 4097, 64, [4097, 1, 2500]),
+    (4, 2, 2, 777, 128, [0, 777, 5, 300]),
+    (2, 4, 4, 2048, 64, [2048, 3]),
+    (1, 7, 2, 129, 128, [129]),
+    (5, 1, 1, 16, 128, [16, 0, 1, 15, 2]),
+]
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_decode_parity(case, dtype, causal, num_splits):
+    B, Sq, H, S_max, D, lens = case
+    say(f"decode B={B} Sq={Sq} H={H} S_max={S_max} D={D} {dtype} causal={causal} "
+        f"splits={num_splits} lens={lens}")
+    inp = synth.decode_inputs(B, Sq, H, S_max, D, dtype, 5000 + S_max + Sq, lens)
+    check(inp, causal, scale_of(D), num_splits)
+
+
+@pytest.mark.parametrize("num_splits", [2, 5, 64, 256, 1000])
+def test_decode_split_counts(num_splits):
+    inp = synth.decode_inputs(2, 1, 2, 3000, 128, "bf16", 5100, [3000, 1234])
+    say(f"decode split count {num_splits}")
+    check(inp, False, scale_of(128), num_splits)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1.0])
+def test_decode_scale_values(scale):
+    inp = synth.decode_inputs(2, 2, 2, 500, 64, "fp16", 5200, [500, 37])
+    say(f"decode scale {scale}")
+    check(inp, True, scale)
+
+
+def test_decode_all_rows_empty():
+    inp = synth.decode_inputs(2, 3, 2, 64, 128, "bf16", 5300, [0, 2])
+    o, lse = run(inp, True, 0.1)     # L < Sq: every row of both sequences sees nothing or little
+    oref, lref = decode_attention(*[synth.bits_to_f64(x, "bf16") for x in (inp.q, inp.k, inp.v)],
+                                  causal=True, scale=0.1, seqlens_k=inp.seqlens)
+    assert torch.equal(o[0], torch.zeros_like(o[0]))
+    assert torch.isneginf(lse[0]).all()
+    assert np.array_equal(np.isneginf(lse.cpu().numpy()), np.isneginf(lref))
+
+
+def test_decode_without_lse_and_determinism():
+    inp = synth.decode_inputs(2, 1, 4, 5000, 128, "bf16", 5400, None)
+    o1, _ = run(inp, False, 0.09, with_lse=False)
+    o2, l2 = run(inp, False, 0.09)
+    assert torch.equal(o1, o2)
+
+
+def test_decode_matches_forward_last_rows():
+    """Sq = L under causality is the causal forward over those L tokens."""
+    B, H, L, D = 2, 2, 300, 128
+    inp = synth.decode_inputs(B, L, H, L, D, "bf16", 5500, None)
+    o_dec, l_dec = run(inp, True, scale_of(D))
+    k = to_dev(np.ascontiguousarray(inp.k.transpose(0, 2, 1, 3)), "bf16")
+    v = to_dev(np.ascontiguousarray(inp.v.transpose(0, 2, 1, 3)), "bf16")
+    o_fwd, l_fwd = binding.fwd(to_dev(inp.q, "bf16"), k, v, causal=True, scale=scale_of(D))
+    torch.cuda.synchronize()
+    assert (o_dec.float() - o_fwd.float()).abs().max().item() <= 2 * TOL_O["bf16"]
+    assert (l_dec - l_fwd).abs().max().item() <= 2 * TOL_LSE
+
+
+@pytest.mark.parametrize("name", list(synth.DECODE_CONFIGS))
+def test_decode_workload_sampled(name):
+    """The benchmark's decode workloads at full size; the oracle checks sampled (b, h) pairs."""
+    cfg = synth.DECODE_CONFIGS[name]
+    say(name, cfg.describe())
+    inp = synth.make_decode_inputs(cfg)
+    o, lse = run(inp, cfg.causal, scale_of(cfg.D))
+    o, lse = o.cpu(), lse.cpu()
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + 3))
+    pairs = {(0, 0), (cfg.B - 1, cfg.H - 1)} | {(int(rng.integers(cfg.B)), int(rng.integers(cfg.H)))
+                                               for _ in range(6)}
+    worst_o = worst_l = 0.0
+    for b, h in sorted(pairs):
+        sl = None if inp.seqlens is None else inp.seqlens[b:b + 1]
+        f = [synth.bits_to_f64(x, cfg.dtype) for x in (inp.q[b:b + 1, :, h:h + 1],
+                                                     inp.k[b:b + 1, h:h + 1], inp.v[b:b + 1, h:h + 1])]
+        oref, lref = decode_attention(*f, causal=cfg.causal, scale=scale_of(cfg.D), seqlens_k=sl)
+        worst_o = max(worst_o, max_abs(o[b:b + 1, :, h:h + 1].float().numpy(), oref))
+        worst_l = max(worst_l, max_abs(lse[b:b + 1, h:h + 1].numpy(), lref))
+    say(f"    sampled {len(pairs)} (b,h): max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O[cfg.dtype] and worst_l <= TOL_LSE
