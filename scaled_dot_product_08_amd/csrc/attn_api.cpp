@@ -58,7 +58,7 @@ int validate(const void* q, const void* k, const void* v, void* out, const float
 // Validation of attn_decode's arguments; no HIP call. Fills the split plan.
 int validate_decode(const void* q, const void* k, const void* v, void* out, const float* lse,
                     int B, int H, int Sq, int S_max, int D, float scale, int dtype,
-                    int num_splits, sdpa08::DecodePlan* plan) {
+                    int num_splits, bool ragged, sdpa08::DecodePlan* plan) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return ATTN_ERR_NULL;
   if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
@@ -71,7 +71,7 @@ int validate_decode(const void* q, const void* k, const void* v, void* out, cons
   if ((long long)S_max * D * 2 + (1LL << 20) > (long long)UINT32_MAX) return ATTN_ERR_SHAPE;
   const long double elems = (long double)B * H * ((long double)S_max + Sq) * D;
   if (elems > (long double)LLONG_MAX / 2) return ATTN_ERR_SHAPE;
-  *plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits);
+  *plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits, ragged);
   const long long rows = (long long)B * H * Sq;
   if (rows * plan->n_splits > INT_MAX) return ATTN_ERR_SHAPE;
   return ATTN_OK;
@@ -183,7 +183,9 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
 
 size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int num_splits) {
   if (B < 0 || H < 1 || Sq < 0 || S_max < 0 || num_splits < 0 || (D != 64 && D != 128)) return 0;
-  const sdpa08::DecodePlan plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits);
+  // Sized for the ragged plan, which has at least as many splits as the
+  // full-cache one: one size serves calls with and without seqlens_k.
+  const sdpa08::DecodePlan plan = sdpa08::decode_plan(B, H, Sq, S_max, D, num_splits, true);
   return decode_workspace_bytes((long long)B * H * Sq, plan, D);
 }
 
@@ -193,7 +195,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 void* workspace, size_t workspace_bytes, void* stream) {
   sdpa08::DecodePlan plan{1, 0};
   const int st = validate_decode(q, k_cache, v_cache, out, lse, B, H, Sq, S_max, D, scale, dtype,
-                                 num_splits, &plan);
+                                 num_splits, seqlens_k != nullptr, &plan);
   if (st != ATTN_OK) return st;
   if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
   const long long rows = (long long)B * H * Sq;

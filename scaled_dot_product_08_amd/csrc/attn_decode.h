@@ -29,7 +29,9 @@ struct DecodePlan {
   int chunk;
 };
 
-DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_req);
+// `ragged`: per-sequence lengths are given (finer splits). A ragged plan
+// never has fewer splits than the full-cache plan of the same shapes.
+DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_req, bool ragged);
 
 hipError_t launch_decode(const DecodeParams& p, int D, bool bf16, hipStream_t stream);
 

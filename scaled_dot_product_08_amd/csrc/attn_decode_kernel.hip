@@ -14,7 +14,9 @@
 //   * Inside a workgroup a cache row (D 16-bit values) is read by D/8 lanes,
 //     16 bytes each, so one wave-wide 16-byte load covers 64/(D/8) whole rows
 //     and the four waves together read one contiguous stretch of the cache.
-//     Each lane keeps eight loads of K and eight of V in flight.
+//     Each lane keeps sixteen loads of K and sixteen of V in flight, marked
+//     non-temporal (the cache is read once; measured 12 % faster than
+//     default-policy loads on MI355X).
 //   * Score: four packed dot2 operations per lane, then a butterfly sum over
 //     the D/8 lanes of the row (DPP quad permutations and row mirrors, no LDS).
 //     Every lane of the group ends with the full score.
@@ -41,8 +43,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+#ifndef SDPA_DEC_UNROLL
+#define SDPA_DEC_UNROLL 16
+#endif
+#ifndef SDPA_DEC_AUX
+#define SDPA_DEC_AUX 2      // non-temporal: the cache is streamed once
+#endif
+
 constexpr int NWAVE = 4;          // waves per workgroup
-constexpr int UNROLL = 8;         // cache-row steps per wave per iteration (loads in flight)
+constexpr int UNROLL = SDPA_DEC_UNROLL;   // cache-row steps per wave per iteration (loads in flight)
+constexpr int LOAD_AUX = SDPA_DEC_AUX;    // cache policy bits of the cache loads
 constexpr int NXCD = 8;           // workgroups go round-robin over the 8 XCDs
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 constexpr int BUF_FLAGS = 0x00020000;   // raw buffer descriptor word 3 (32-bit dwords)
@@ -170,12 +180,12 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_decode_split_kernel(DecodePar
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const uint32_t off = (uint32_t)(kb + u * G::KPW + grp) * G::ROWB + sub * 16;
-      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, LOAD_AUX);
     }
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       const uint32_t off = (uint32_t)(kb + u * G::KPW + grp) * G::ROWB + sub * 16;
-      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, LOAD_AUX);
     }
 
     float t[UNROLL];
@@ -293,17 +303,19 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_req) {
+DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_req, bool ragged) {
   const int keys_wg = (D == 64) ? Geo<64>::KEYS_WG : Geo<128>::KEYS_WG;
   const long long rows = (long long)B * H * Sq;
   long long n;
   if (num_splits_req > 0) {
     n = num_splits_req;
   } else {
-    // Aim for about 2048 workgroups (8 per CU), each with at least four
-    // iterations of its loop.
-    const long long target = 2048;
-    const long long min_keys = 4LL * keys_wg;
+    // Full caches: about 2048 workgroups (8 per CU). Ragged lengths (known
+    // only on the device): 8x finer splits, so the splits past a short
+    // sequence's end exit at once and the long ones do not leave a tail.
+    // Every split covers at least two iterations of the workgroup loop.
+    const long long target = ragged ? 16384 : 2048;
+    const long long min_keys = 2LL * keys_wg;
     const long long by_size = ((long long)S_max + min_keys - 1) / min_keys;
     const long long want = rows > 0 ? (target + rows - 1) / rows : 1;
     n = want < by_size ? want : by_size;
