@@ -25,11 +25,13 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak bandwidth
 KERNEL_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_fwd_kernel.hip",
                   "scaled_dot_product_08_amd/csrc/attn_kernel.h"]
+DECODE_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_decode_kernel.hip",
+                  "scaled_dot_product_08_amd/csrc/attn_decode.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (sources or KERNEL_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -138,10 +140,12 @@ def time_decode(cfg, steps: int, warmup: int):
     return {"workload": cfg.describe(), "us_per_call": round(ms * 1e3, 2),
             "algorithmic_bytes": nbytes, "GB_per_s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "tflops": round(accounting.decode_flops(cfg.H, cfg.Sq, cfg.D, lens) / (ms * 1e-3) / 1e12, 2)}
+            "tflops": round(accounting.decode_flops(cfg.H, cfg.Sq, cfg.D, lens) / (ms * 1e-3) / 1e12, 2),
+            "traffic": read_traffic(cfg.name, DECODE_SOURCES),
+            "kernel_source": kernel_source_hash(DECODE_SOURCES)}
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
@@ -150,7 +154,7 @@ def read_traffic(workload: str):
         rec = json.load(open(path))
     except Exception:
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -200,6 +204,35 @@ def cpu_baseline(cfg, budget_s: float = 12.0):
             "sample": f"{done} full (sequence, head) slices of S={S} rows (all keys each row sees), fp64 numpy, {dt:.1f} s"}
 
 
+def calibration_copy(mib: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"  calibration copy: {mib} MiB x 3")
+
+
+def side(args, synth):
+    """One side figure on its own (used for its rocprofv3 summaries)."""
+    name = args.side
+    if name in synth.DECODE_CONFIGS:
+        r = time_decode(synth.DECODE_CONFIGS[name], args.steps, args.warmup)
+    else:
+        c = synth.CONFIGS[name]
+        r2 = time_workload(c, args.steps, args.warmup)
+        r = {"workload": c.describe(), "us_per_call": round(r2["ms"] * 1e3, 2),
+             "tflops": round(r2["tflops"], 1), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4)}
+    log(f"  {name}: {r}")
+    calibration_copy(args.calib_copy_mib)
+    print(json.dumps({"side": name, "steps": args.steps, "warmup": args.warmup, **r}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +241,9 @@ def main():
     ap.add_argument("--workload", default="llama", help="key of synth.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the side figures (B4 H12 S2048 D64, ALiBi, 128K window)")
+    ap.add_argument("--side", default=None,
+                    help="time only this side figure (a key of synth.CONFIGS or synth.DECODE_CONFIGS) "
+                         "and print it as one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -225,6 +261,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     binding.load_library()
+    if args.side is not None:
+        side(args, synth)
+        return
     cfg = synth.CONFIGS[args.workload]
     log(f"workload {cfg.describe()}: warmup {args.warmup}, steps {args.steps}")
     r = time_workload(cfg, args.steps, args.warmup)
@@ -247,14 +286,7 @@ def main():
             log(f"  {name}: {r3['us_per_call']:.1f} us, {r3['GB_per_s']:.0f} GB/s "
                 f"({100 * r3['frac_of_hbm_peak']:.1f} % of HBM peak)")
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"  calibration copy: {args.calib_copy_mib} MiB x 3")
+    calibration_copy(args.calib_copy_mib)
 
     traffic = read_traffic(args.workload)
     line = {
