@@ -42,7 +42,7 @@ enum {
   ATTN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
   ATTN_ERR_SEQLENS = -7,     /* cu_seqlens failed validation (debug check) */
   ATTN_ERR_ALIGN = -8,       /* a tensor pointer is not 16-byte aligned */
-  ATTN_ERR_WORKSPACE = -9    /* attn_decode: workspace NULL or too small */
+  ATTN_ERR_WORKSPACE = -9    /* attn_decode / attn_bwd: workspace NULL or too small */
 };
 
 /*
@@ -152,6 +152,34 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
                 int S_max, int D, int causal, float scale, int dtype, int num_splits,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd with respect to q, k and v.
+ *
+ * The backward(grad_output) step that mlqm.cn/news/343191 §3.3 reserves for
+ * the fused operation: given the forward's inputs, its output `out` and its
+ * log-sum-exp `lse`, and the gradient `dout` of a loss with respect to out,
+ *   dv = P^T dout,  dS = P * (dout v^T - rowsum(dout * out)),
+ *   dq = scale * dS k,  dk = scale * dS^T q,
+ * per (sequence, head), with P recomputed from q, k and lse tile by tile
+ * (it never reaches memory). Masks and layouts are attn_fwd's (padded
+ * (B, S, H, D) or packed (T, H, D) with cu_seqlens; lse (B, H, S) or (H, T),
+ * REQUIRED here). dout, dq, dk, dv have q's layout and dtype; dq, dk, dv are
+ * written (rounded to nearest even) and must not overlap the inputs.
+ *   workspace : DEVICE memory of attn_bwd_workspace_size(B, H, S, packed)
+ *               bytes (one fp32 per row and head), 16-byte aligned, owned by
+ *               the caller, used until the stream passes the call.
+ * Two kernels run on `stream`: dq (which also fills the workspace with
+ * rowsum(dout * out)), then dk and dv. No atomics: results are
+ * deterministic. Errors as attn_fwd, plus ATTN_ERR_NULL for a missing lse,
+ * dout, dq, dk or dv and ATTN_ERR_WORKSPACE.
+ */
+size_t attn_bwd_workspace_size(int B, int H, int S, int packed);
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
+             int causal, float scale, int dtype, const int32_t* cu_seqlens, void* workspace,
+             size_t workspace_bytes, void* stream);
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* attn_strerror(int status);

@@ -18,8 +18,8 @@ STATUS = {
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_decode", "attn_decode_workspace_size", "attn_strerror",
-           "attn_check_cu_seqlens", "attn_version")
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+           "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -48,6 +48,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
          ctypes.c_void_p]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+         ctypes.c_void_p]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 4
     lib.attn_decode.restype = ctypes.c_int
     lib.attn_decode.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
@@ -95,6 +101,19 @@ def attn_decode_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq
                                       int(H), int(Sq), int(S_max), int(D), int(causal),
                                       float(scale), int(dtype), int(num_splits), ws_ptr,
                                       int(ws_bytes), stream_ptr)
+
+
+def attn_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, S, D,
+                 causal, scale, dtype, cu_ptr, ws_ptr, ws_bytes, stream_ptr) -> int:
+    """Direct call of attn_bwd with integer pointers; returns the status code."""
+    return load_library().attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                   dv_ptr, int(B), int(H), int(S), int(D), int(causal),
+                                   float(scale), int(dtype), cu_ptr, ws_ptr, int(ws_bytes),
+                                   stream_ptr)
+
+
+def bwd_workspace_size(B, H, S, packed=False) -> int:
+    return int(load_library().attn_bwd_workspace_size(int(B), int(H), int(S), int(bool(packed))))
 
 
 def decode_workspace_size(B, H, Sq, S_max, D, num_splits=0) -> int:
@@ -234,3 +253,41 @@ def decode(q, k_cache, v_cache, *, seqlens_k=None, causal: bool = False, scale: 
     attn_decode(q, k_cache, v_cache, out, lse, seqlens_k=seqlens_k, causal=causal, scale=scale,
                 num_splits=num_splits, stream=stream)
     return out, lse
+
+
+def attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, *, causal: bool, scale: float | None = None,
+             cu_seqlens=None, workspace=None, stream=None) -> None:
+    """Call attn_bwd on torch device tensors (layouts as attn_fwd; lse required)."""
+    import torch
+    for t in (q, k, v, out, dout, dq, dk, dv):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if cu_seqlens is None:
+        B, S, H, D = q.shape
+        cu_ptr = None
+    else:
+        T, H, D = q.shape
+        B, S = cu_seqlens.numel() - 1, T
+        cu_ptr = cu_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = bwd_workspace_size(B, H, S, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, S, D,
+                      int(bool(causal)), scale, _dtype_code(q), cu_ptr, workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+
+
+def bwd(q, k, v, out, lse, dout, *, causal: bool, scale: float | None = None, cu_seqlens=None,
+        stream=None):
+    """Allocate dQ, dK, dV with torch and run attn_bwd. Returns (dq, dk, dv)."""
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, causal=causal, scale=scale,
+             cu_seqlens=cu_seqlens, stream=stream)
+    return dq, dk, dv
+

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/attn.h"
+#include "attn_bwd.h"
 #include "attn_decode.h"
 #include "attn_kernel.h"
 
@@ -222,6 +223,59 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   p.causal = causal != 0;
   const hipError_t e = sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16,
                                              reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t attn_bwd_workspace_size(int B, int H, int S, int packed) {
+  if (H < 1 || S < 0 || B < 0) return 0;
+  const long long rows = packed ? (long long)S : (long long)B * S;
+  return (size_t)rows * H * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int H, int S, int D,
+             int causal, float scale, int dtype, const int32_t* cu_seqlens, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  long long grid = 0;
+  // q, k, v and out are checked like the forward's (out is an input here).
+  const int st = validate(q, k, v, const_cast<void*>(out), lse, B, H, S, D, scale, dtype,
+                          cu_seqlens, &grid);
+  if (st != ATTN_OK) return st;
+  if (lse == nullptr || dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr) {
+    return ATTN_ERR_NULL;
+  }
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) {
+    return ATTN_ERR_ALIGN;
+  }
+  const bool packed = cu_seqlens != nullptr;
+  const size_t need = attn_bwd_workspace_size(B, H, S, packed ? 1 : 0);
+  if (S == 0 || (packed && B == 0)) return ATTN_OK;
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  if (packed && debug_enabled()) {
+    const int c = attn_check_cu_seqlens(cu_seqlens, B, S, stream);
+    if (c != ATTN_OK) return c;
+  }
+  sdpa08::BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(out);
+  p.dout = static_cast<const uint16_t*>(dout);
+  p.lse = lse;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.delta = static_cast<float*>(workspace);
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.S = S;
+  p.n_tiles = 0;
+  p.c_log2 = scale * 1.4426950408889634f;
+  p.scale = scale;
+  const hipError_t e = sdpa08::launch_bwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
+                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -126,3 +126,30 @@ def test_decode_workspace_size_rules(lib):
 def test_decode_empty_problem_is_noop():
     assert call_dec(B=0) == 0
     assert call_dec(Sq=0) == 0
+
+
+def call_bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, S=128, D=128, causal=0,
+             scale=0.1, dtype=binding.ATTN_DTYPE_BF16, cu=None, ws=None, wsb=0)
+    a.update(kw)
+    return binding.attn_bwd_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                a["dv"], a["B"], a["H"], a["S"], a["D"], a["causal"], a["scale"],
+                                a["dtype"], a["cu"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(do=None), -1),
+    (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(dtype=7), -3), (dict(D=32), -5), (dict(scale=float("nan")), -4), (dict(H=0), -2),
+    (dict(do=P + 8), -8), (dict(dv=P + 2), -8), (dict(lse=P + 1), -8),
+    (dict(), -9), (dict(ws=P, wsb=2 * 128 * 4 - 1), -9), (dict(ws=P + 4, wsb=1 << 20), -8),
+])
+def test_bwd_argument_errors(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_workspace_and_empty(lib):
+    assert binding.bwd_workspace_size(2, 3, 100, False) == 2 * 3 * 100 * 4
+    assert binding.bwd_workspace_size(5, 3, 100, True) == 3 * 100 * 4
+    assert call_bwd(S=0) == 0
+    assert call_bwd(B=0, cu=P, S=10) == 0
