@@ -54,6 +54,12 @@ def masked_flops(B: int, H: int, L: int, D: int, causal: bool, window: int = 0,
     return 4.0 * D * B * H * visible_pairs(L, causal, window, n_global)
 
 
+# The backward's algorithmic work: five products of the forward's size (the
+# recomputed Q K^T, dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q) against
+# the forward's two, i.e. 2.5x the forward count.
+BACKWARD_FLOP_RATIO = 2.5
+
+
 def qkv_read_bytes(B: int, H: int, S: int, D: int, dtype: str = "fp16") -> int:
     return 3 * B * H * S * D * ELEM_BYTES[dtype]
 

@@ -376,8 +376,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // V^T (64 registers) and the dK^T, dV^T accumulators (128) besides the
 // score blocks, more than the 256 registers two waves per SIMD allow, so
 // that instance runs one wave per SIMD.
+#ifndef SDPA_BWD_DKDV_WAVES_128
+#define SDPA_BWD_DKDV_WAVES_128 1
+#endif
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64, D == 128 ? 1 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   using O = Offsets<D>;
   constexpr int ROWB = O::ROWB, TILEB = O::TILEB, LDW = O::LDW, DCH = O::DCH, DB = O::DB;
   constexpr int STAGEB = 2 * TILEB + 2048;   // Q tile + dO tile + 1 KB LSE + 1 KB delta
