@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (B4 H12 S2048 D64 fp16; S4096 D128 bf16)"
 PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak bandwidth
+PEAK_TFLOPS_FP8 = 5033.2      # MI355X dense fp8 MFMA: twice the fp16/bf16 rate
 KERNEL_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_fwd_kernel.hip",
                   "scaled_dot_product_08_amd/csrc/attn_kernel.h"]
 DECODE_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_decode_kernel.hip",
@@ -98,6 +99,47 @@ def time_workload(cfg, steps: int, warmup: int):
     ms = t0.elapsed_time(t1) / steps
     return {"ms": ms, "flops": fl, "bytes": nbytes, "tflops": fl / (ms * 1e-3) / 1e12,
             "sha256": inp.sha256}
+
+
+def time_fp8(cfg, steps: int, warmup: int):
+    """attn_fwd_fp8 on E4M3 inputs of a forward workload's shape (bf16 output)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from scaled_dot_product_08_amd import accounting, binding
+
+    q8, k8, v8 = (torch.from_numpy(x).cuda()
+                  for x in synth.fp8_qkv((cfg.B, cfg.S, cfg.H, cfg.D), cfg.seed + 9, cfg.mult))
+    scale = float(np.float32(1.0 / math.sqrt(cfg.D)))
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.B, cfg.H, cfg.S), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fl = accounting.flops(cfg.B, cfg.H, cfg.S, cfg.D, cfg.causal)
+
+    def step():
+        st = binding.attn_fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), cfg.B, cfg.H, cfg.S, cfg.D, int(cfg.causal),
+                                      scale, 1.0, 1.0, 1.0, binding.ATTN_DTYPE_BF16, None,
+                                      stream.cuda_stream)
+        if st != 0:
+            raise binding.AttnError(st, binding.attn_strerror(st))
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": cfg.describe().replace(cfg.dtype, "e4m3 (bf16 out)"),
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tf, 1),
+            "frac_of_fp8_peak": round(tf / PEAK_TFLOPS_FP8, 4)}
 
 
 def time_backward(cfg, steps: int, warmup: int):
@@ -268,6 +310,8 @@ def side(args, synth):
     name = args.side
     if name in synth.DECODE_CONFIGS:
         r = time_decode(synth.DECODE_CONFIGS[name], args.steps, args.warmup)
+    elif name.endswith("_fp8"):
+        r = time_fp8(synth.CONFIGS[name[:-4]], args.steps, args.warmup)
     elif name.endswith("_bwd"):
         r = time_backward(synth.CONFIGS[name[:-4]], args.steps, args.warmup)
     else:
@@ -327,6 +371,9 @@ def main():
             log(f"  {name}: {r2['ms'] * 1e3:.1f} us, {r2['tflops']:.1f} TFLOP/s")
 
     if not args.no_extra:
+        r5 = time_fp8(synth.CONFIGS["llama"], max(100, args.steps), max(100, args.warmup))
+        also["llama_fp8"] = r5
+        log(f"  llama_fp8: {r5['us_per_call']:.1f} us, {r5['tflops']:.1f} TFLOP/s")
         for name in ("llama", "mha"):
             r4 = time_backward(synth.CONFIGS[name], max(50, args.steps // 2), max(20, args.warmup // 5))
             also[name + "_bwd"] = r4

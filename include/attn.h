@@ -114,6 +114,27 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                  const float* alibi_slopes, void* stream);
 
 /*
+ * attn_fwd_fp8 -- attn_fwd on FP8 inputs.
+ *
+ * jianying88.com/news/49672 §3 mentions FP8 attention (less memory, a small
+ * speed gain); this is that variant for D = 128: q, k, v hold OCP E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 448 the largest
+ * finite value), one byte per element, in attn_fwd's layouts; each tensor
+ * carries one float scale, so the operation is
+ *   out = softmax(scale * (descale_q Q)(descale_k K)^T + mask) (descale_v V).
+ * out is written in `out_dtype` (ATTN_DTYPE_BF16 or ATTN_DTYPE_FP16), lse in
+ * fp32 as attn_fwd. Both products run on the 8-bit matrix core with fp32
+ * accumulation; the probabilities are rounded to E4M3 (after scaling by
+ * 2^4) for the P V product, so O carries up to 2^-4 relative error per term
+ * of its weighted sum (the LSE does not: it sums the fp32 probabilities).
+ * D other than 128 -> ATTN_ERR_UNSUPPORTED; a non-finite descale or scale
+ * product -> ATTN_ERR_SCALE. Other arguments and errors as attn_fwd.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int H, int S, int D, int causal, float scale, float descale_q, float descale_k,
+                 float descale_v, int out_dtype, const int32_t* cu_seqlens, void* stream);
+
+/*
  * attn_decode -- attention of a few new query rows against a KV cache.
  *
  * The decode step of autoregressive generation: the cache holds keys and

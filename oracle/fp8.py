@@ -68,9 +68,10 @@ def e4m3_encode(x) -> np.ndarray:
 
 
 def attention_fp8(q8, k8, v8, *, descale_q: float, descale_k: float, descale_v: float,
-                  causal: bool, scale: float, cu_seqlens=None):
+                  causal: bool, scale: float, cu_seqlens=None, return_probs: bool = False):
     """Attention forward on E4M3 codes with per-tensor descales (layouts as oracle.attention)."""
     q = e4m3_decode(q8) * float(descale_q)
     k = e4m3_decode(k8) * float(descale_k)
     v = e4m3_decode(v8) * float(descale_v)
-    return attention(q, k, v, causal=causal, scale=scale, cu_seqlens=cu_seqlens)
+    return attention(q, k, v, causal=causal, scale=scale, cu_seqlens=cu_seqlens,
+                     return_probs=return_probs)

@@ -18,7 +18,7 @@ STATUS = {
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
@@ -48,6 +48,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
          ctypes.c_void_p]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float] * 4 + \
+        [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
@@ -101,6 +104,14 @@ def attn_decode_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq
                                       int(H), int(Sq), int(S_max), int(D), int(causal),
                                       float(scale), int(dtype), int(num_splits), ws_ptr,
                                       int(ws_bytes), stream_ptr)
+
+
+def attn_fwd_fp8_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dq, dk, dv,
+                     out_dtype, cu_ptr, stream_ptr) -> int:
+    """Direct call of attn_fwd_fp8 with integer pointers; returns the status code."""
+    return load_library().attn_fwd_fp8(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
+                                       int(D), int(causal), float(scale), float(dq), float(dk),
+                                       float(dv), int(out_dtype), cu_ptr, stream_ptr)
 
 
 def attn_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, S, D,
@@ -290,4 +301,34 @@ def bwd(q, k, v, out, lse, dout, *, causal: bool, scale: float | None = None, cu
     attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, causal=causal, scale=scale,
              cu_seqlens=cu_seqlens, stream=stream)
     return dq, dk, dv
+
+
+def fwd_fp8(q8, k8, v8, *, causal: bool, scale: float | None = None, descale_q: float = 1.0,
+            descale_k: float = 1.0, descale_v: float = 1.0, out_dtype=None, cu_seqlens=None,
+            with_lse: bool = True, stream=None):
+    """attn_fwd_fp8 on uint8 device tensors of E4M3 codes. Returns (O, LSE or None)."""
+    import torch
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors of E4M3 codes")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    out = torch.empty(q8.shape, dtype=out_dtype, device=q8.device)
+    if cu_seqlens is None:
+        B, S, H, D = q8.shape
+        cu_ptr = None
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q8.device) if with_lse else None
+    else:
+        T, H, D = q8.shape
+        B, S = cu_seqlens.numel() - 1, T
+        cu_ptr = cu_seqlens.data_ptr()
+        lse = torch.empty((H, T), dtype=torch.float32, device=q8.device) if with_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = attn_fwd_fp8_raw(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                          None if lse is None else lse.data_ptr(), B, H, S, D, int(bool(causal)),
+                          scale, descale_q, descale_k, descale_v, _dtype_code(out), cu_ptr,
+                          _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
+    return out, lse
 

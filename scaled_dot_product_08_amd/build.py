@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsdpa08.so")
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip",
+           "attn_decode_kernel.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code.

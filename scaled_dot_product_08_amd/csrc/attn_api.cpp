@@ -13,6 +13,7 @@
 #include "../../include/attn.h"
 #include "attn_bwd.h"
 #include "attn_decode.h"
+#include "attn_fp8.h"
 #include "attn_kernel.h"
 
 namespace {
@@ -276,6 +277,52 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.scale = scale;
   const hipError_t e = sdpa08::launch_bwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                 int H, int S, int D, int causal, float scale, float descale_q, float descale_k,
+                 float descale_v, int out_dtype, const int32_t* cu_seqlens, void* stream) {
+  long long grid = 0;
+  const int st = validate(q, k, v, out, lse, B, H, S, D, scale, out_dtype, cu_seqlens, &grid);
+  if (st != ATTN_OK) return st;
+  if (D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!std::isfinite(descale_q) || !std::isfinite(descale_k) || !std::isfinite(descale_v)) {
+    return ATTN_ERR_SCALE;
+  }
+  const float eff = scale * descale_q * descale_k;
+  if (!std::isfinite(eff)) return ATTN_ERR_SCALE;
+  const bool packed = cu_seqlens != nullptr;
+  if (S == 0 || (packed && B == 0)) return ATTN_OK;
+  if (packed && debug_enabled()) {
+    const int c = attn_check_cu_seqlens(cu_seqlens, B, S, stream);
+    if (c != ATTN_OK) return c;
+  }
+  sdpa08::Fp8Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.B = B;
+  p.H = H;
+  p.S = S;
+  p.n_qtiles = 0;
+  const float log2e = 1.4426950408889634f;
+  if (eff > 0.0f) {
+    p.c_log2 = eff * log2e;
+    p.q_mode = 0;
+  } else if (eff < 0.0f) {
+    p.c_log2 = -eff * log2e;
+    p.q_mode = 1;
+  } else {
+    p.c_log2 = log2e;
+    p.q_mode = 2;
+  }
+  p.v_descale = descale_v;
+  const hipError_t e = sdpa08::launch_fwd_fp8(p, out_dtype == ATTN_DTYPE_BF16, causal != 0, packed,
+                                              reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

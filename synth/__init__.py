@@ -57,6 +57,20 @@ def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def fp8_qkv(shape, seed: int, mult: float = 1.0):
+    """Q, K, V as OCP E4M3 codes (uint8) of i.i.d. N(0,1)*mult values, rounded to
+    nearest even by torch's float8_e4m3fn conversion."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+        if mult != 1.0:
+            x *= np.float32(mult)
+        out.append(torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    return tuple(out)
+
+
 def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Decode fp16/bf16 bit patterns (uint16) exactly to float64."""
     bits = np.ascontiguousarray(bits, dtype=np.uint16)

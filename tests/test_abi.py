@@ -153,3 +153,25 @@ def test_bwd_workspace_and_empty(lib):
     assert binding.bwd_workspace_size(5, 3, 100, True) == 3 * 100 * 4
     assert call_bwd(S=0) == 0
     assert call_bwd(B=0, cu=P, S=10) == 0
+
+
+def call_fp8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=2, S=128, D=128, causal=0, scale=0.1, dq=1.0,
+             dk=1.0, dv=1.0, od=binding.ATTN_DTYPE_BF16, cu=None)
+    a.update(kw)
+    return binding.attn_fwd_fp8_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["S"],
+                                    a["D"], a["causal"], a["scale"], a["dq"], a["dk"], a["dv"],
+                                    a["od"], a["cu"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(od=3), -3), (dict(D=64), -5), (dict(D=96), -5),
+    (dict(dq=float("inf")), -4), (dict(dv=float("nan")), -4), (dict(scale=1e30, dq=1e30), -4),
+    (dict(k=P + 8), -8), (dict(H=0), -2),
+])
+def test_fp8_argument_errors(kw, code):
+    assert call_fp8(**kw) == code
+
+
+def test_fp8_empty_problem_is_noop():
+    assert call_fp8(S=0) == 0
