@@ -54,8 +54,9 @@ def make_device_inputs(cfg):
     return inp, dev, cu
 
 
-def time_workload(cfg, steps: int, warmup: int):
-    """Median-free mean over ``steps`` back-to-back launches bracketed by events."""
+def time_workload(cfg, steps: int, warmup: int, samples: int = 0):
+    """Mean over ``steps`` back-to-back launches bracketed by events; with ``samples``,
+    also that many individually timed launches afterwards (median and minimum)."""
     import numpy as np
     import torch
 
@@ -97,8 +98,37 @@ def time_workload(cfg, steps: int, warmup: int):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    return {"ms": ms, "flops": fl, "bytes": nbytes, "tflops": fl / (ms * 1e-3) / 1e12,
-            "sha256": inp.sha256}
+    res = {"ms": ms, "flops": fl, "bytes": nbytes, "tflops": fl / (ms * 1e-3) / 1e12,
+           "sha256": inp.sha256}
+    if samples > 0:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(samples)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        res["per_launch_us"] = {"samples": samples, "median": round(per[len(per) // 2], 2),
+                                "min": round(per[0], 2)}
+    return res
+
+
+def device_peak():
+    """CUs x 4096 FLOP/clk x the device's maximum shader clock, from the HIP runtime."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+        # hipDeviceAttributeMultiprocessorCount = 63, hipDeviceAttributeClockRate = 5 (kHz)
+        if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0) != 0:
+            return None
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:
+            return None
+        return {"cus": cus.value, "max_sclk_mhz": khz.value / 1e3,
+                "tflops": round(cus.value * 4096 * khz.value * 1e3 / 1e12, 1)}
+    except OSError:
+        return None
 
 
 def time_fp8(cfg, steps: int, warmup: int):
@@ -357,17 +387,20 @@ def main():
         return
     cfg = synth.CONFIGS[args.workload]
     log(f"workload {cfg.describe()}: warmup {args.warmup}, steps {args.steps}")
-    r = time_workload(cfg, args.steps, args.warmup)
-    log(f"  {r['ms'] * 1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s")
+    r = time_workload(cfg, args.steps, args.warmup, samples=20)
+    log(f"  {r['ms'] * 1e3:.1f} us/step, {r['tflops']:.1f} TFLOP/s; per launch {r['per_launch_us']}")
 
     also = {}
     if not args.no_extra:
-        for name in ("mha", "mha_causal", "llama_alibi", "window128k"):
+        for name in ("tiny", "mha", "mha_causal", "long", "varlen", "llama_alibi", "window128k"):
             c2 = synth.CONFIGS[name]
-            r2 = time_workload(c2, max(100, args.steps), max(100, args.warmup))
+            # launch-bound small problems get more launches; the 64K-token ones fewer
+            n = {"tiny": 1000, "long": 20, "varlen": 50}.get(name, max(100, args.steps))
+            r2 = time_workload(c2, n, min(n, max(20, args.warmup)), samples=20)
             also[name] = {"workload": c2.describe(), "us_per_call": round(r2["ms"] * 1e3, 2),
                           "tflops": round(r2["tflops"], 1),
-                          "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4)}
+                          "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),
+                          "per_launch_us": r2["per_launch_us"]}
             log(f"  {name}: {r2['ms'] * 1e3:.1f} us, {r2['tflops']:.1f} TFLOP/s")
 
     if not args.no_extra:
@@ -406,6 +439,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(r["tflops"], 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(r["tflops"] / PEAK_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_bytes": r["bytes"],
+                     "per_launch_us": r["per_launch_us"], "device_peak": device_peak(),
                      "kernel_source": kernel_source_hash()},
         "also": also,
     }
