@@ -100,7 +100,28 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine the two halves of a wave: lane i gets op(x[i % 32], x[i % 32 + 32]).
+// v_permlane32_swap_b32 a, b exchanges the upper half of a with the lower
+// half of b; with a = b = x, afterwards {a, b} = {x[i % 32], x[i % 32 + 32]}
+// at every lane (measured), in some order, and max and + are symmetric. It is
+// written in assembly because the compiler's model of the builtin's second
+// result folds it into the first; the s_nops on either side cover the
+// VALU-to-permlane and permlane-to-VALU hazards.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
@@ -269,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
       dpart = fmaf(a[1], o2[1], dpart);
     }
   }
-  const float delta = dpart + wave_xor32(dpart);
+  const float delta = half_sum(dpart);
   const float lse2 = (qi < L) ? p.lse[row_base + qi] * LOG2E : 0.0f;
   if (hh == 0 && qi < L) p.delta[row_base + qi] = delta;
   const float c_log2 = p.c_log2;

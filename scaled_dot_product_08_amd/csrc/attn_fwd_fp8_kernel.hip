@@ -83,7 +83,28 @@ __device__ __forceinline__ int swz8(int r) {
   return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine the two halves of a wave: lane i gets op(x[i % 32], x[i % 32 + 32]).
+// v_permlane32_swap_b32 a, b exchanges the upper half of a with the lower
+// half of b; with a = b = x, afterwards {a, b} = {x[i % 32], x[i % 32 + 32]}
+// at every lane (measured), in some order, and max and + are symmetric. It is
+// written in assembly because the compiler's model of the builtin's second
+// result folds it into the first; the s_nops on either side cover the
+// VALU-to-permlane and permlane-to-VALU hazards.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
+    mx = half_max(mx);
     const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
     const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
     if (__builtin_amdgcn_ballot_w64(bump)) {
@@ -316,7 +337,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   }
 
   // ---- epilogue: O = descale_v * acc / l, LSE = (m - 4 + log2 l) ln 2 --------
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   const float f = p.v_descale / l_tot;
   // Register r of block d holds column 32 d + 8 (r / 4) + 4 hh + r % 4: runs
   // of four consecutive columns, stored 8 bytes at a time.

@@ -113,7 +113,28 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine the two halves of a wave: lane i gets op(x[i % 32], x[i % 32 + 32]).
+// v_permlane32_swap_b32 a, b exchanges the upper half of a with the lower
+// half of b; with a = b = x, afterwards {a, b} = {x[i % 32], x[i % 32 + 32]}
+// at every lane (measured), in some order, and max and + are symmetric. It is
+// written in assembly because the compiler's model of the builtin's second
+// result folds it into the first; the s_nops on either side cover the
+// VALU-to-permlane and permlane-to-VALU hazards.
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
@@ -408,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
+    mx = half_max(mx);
     // With ALiBi the scores are already log2-scaled.
     const bool prescaled = EXT && use_alibi;
     const float mx2 = prescaled ? mx : ((mx == -INFINITY) ? -INFINITY : mx * c_log2);
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   }
 
   // ---- epilogue: O = acc / l, LSE = ln(l) + m -------------------------------
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
   // Stores past the sequence end fall outside the descriptor and are dropped.
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(og, q_rows * tok_bytes);
