@@ -393,15 +393,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per 128 keys. With D = 128 a wave holds K^T,
-// V^T (64 registers) and the dK^T, dV^T accumulators (128) besides the
-// score blocks, more than the 256 registers two waves per SIMD allow, so
-// that instance runs one wave per SIMD.
-#ifndef SDPA_BWD_DKDV_WAVES_128
-#define SDPA_BWD_DKDV_WAVES_128 1
+// dK and dV: one workgroup per 128 keys. MODE 0 computes both. With D = 128
+// a wave would hold K^T, V^T (64 registers) and both accumulators (128)
+// besides the score blocks, more than the 256 registers that two waves per
+// SIMD allow; there the work is split over two launches instead, MODE 1
+// (dV only: S, P, dO^T P; no V^T, no dS) and MODE 2 (dK only: S, dP, dS,
+// Q^T dS), each fitting two waves per SIMD, at the price of computing Q K^T
+// twice.
+enum { DKDV_BOTH = 0, DKDV_V = 1, DKDV_K = 2 };
+#ifndef SDPA_BWD_SPLIT_128
+#define SDPA_BWD_SPLIT_128 1
 #endif
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int MODE>
+__global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) void attn_bwd_dkdv_kernel(BwdParams p) {
+  constexpr bool DO_V = MODE != DKDV_K;
+  constexpr bool DO_K = MODE != DKDV_V;
   using O = Offsets<D>;
   constexpr int ROWB = O::ROWB, TILEB = O::TILEB, LDW = O::LDW, DCH = O::DCH, DB = O::DB;
   constexpr int STAGEB = 2 * TILEB + 2048;   // Q tile + dO tile + 1 KB LSE + 1 KB delta
@@ -437,7 +443,9 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) vo
 #pragma unroll
   for (int c = 0; c < DCH; ++c) {
     kreg[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, row_voff + c * 32, 0, 0));
-    vreg[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, row_voff + c * 32, 0, 0));
+    if constexpr (DO_K) {
+      vreg[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, row_voff + c * 32, 0, 0));
+    }
   }
   const float c_log2 = p.c_log2;
   const O off(wave, lane, tok_bytes);
@@ -491,8 +499,10 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) vo
       for (int c = 0; c < DCH; ++c) {
         const u32x4 qa = *reinterpret_cast<const u32x4*>(qs + kb * 32 * ROWB + off.a_off[c]);
         s = mfma32<BF16>(qa, kreg[c], s);
-        const u32x4 da = *reinterpret_cast<const u32x4*>(dos + kb * 32 * ROWB + off.a_off[c]);
-        dp = mfma32<BF16>(da, vreg[c], dp);
+        if constexpr (DO_K) {
+          const u32x4 da = *reinterpret_cast<const u32x4*>(dos + kb * 32 * ROWB + off.a_off[c]);
+          dp = mfma32<BF16>(da, vreg[c], dp);
+        }
       }
 
       const bool need_mask = (qb0 + 32 > L) || (CAUSAL && qb0 < wk0 + 31);
@@ -513,24 +523,32 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) vo
             if (!(qrow < L && (!CAUSAL || qrow >= ki))) pr = 0.0f;
           }
           pv[e] = pr;
-          dv[e] = pr * (dp[r] - d4[e]);
+          if constexpr (DO_K) dv[e] = pr * (dp[r] - d4[e]);
         }
-        pp[2 * g] = pack2<BF16>(pv[0], pv[1]);
-        pp[2 * g + 1] = pack2<BF16>(pv[2], pv[3]);
-        pd[2 * g] = pack2<BF16>(dv[0], dv[1]);
-        pd[2 * g + 1] = pack2<BF16>(dv[2], dv[3]);
+        if constexpr (DO_V) {
+          pp[2 * g] = pack2<BF16>(pv[0], pv[1]);
+          pp[2 * g + 1] = pack2<BF16>(pv[2], pv[3]);
+        }
+        if constexpr (DO_K) {
+          pd[2 * g] = pack2<BF16>(dv[0], dv[1]);
+          pd[2 * g + 1] = pack2<BF16>(dv[2], dv[3]);
+        }
       }
 
       // dV^T += dO^T P and dK^T += Q^T dS over two 16-row steps.
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int kc = 2 * kb + e;
-        const u32x4 bp = {pp[e * 4 + 0], pp[e * 4 + 1], pp[e * 4 + 2], pp[e * 4 + 3]};
-        const u32x4 bd = {pd[e * 4 + 0], pd[e * 4 + 1], pd[e * 4 + 2], pd[e * 4 + 3]};
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          acc_v[d] = mfma32<BF16>(read_t<D>(dos, off, kc, d), bp, acc_v[d]);
-          acc_k[d] = mfma32<BF16>(read_t<D>(qs, off, kc, d), bd, acc_k[d]);
+          if constexpr (DO_V) {
+            const u32x4 bp = {pp[e * 4 + 0], pp[e * 4 + 1], pp[e * 4 + 2], pp[e * 4 + 3]};
+            acc_v[d] = mfma32<BF16>(read_t<D>(dos, off, kc, d), bp, acc_v[d]);
+          }
+          if constexpr (DO_K) {
+            const u32x4 bd = {pd[e * 4 + 0], pd[e * 4 + 1], pd[e * 4 + 2], pd[e * 4 + 3]};
+            acc_k[d] = mfma32<BF16>(read_t<D>(qs, off, kc, d), bd, acc_k[d]);
+          }
         }
       }
     }
@@ -556,8 +574,8 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? SDPA_BWD_DKDV_WAVES_128 : 2) vo
 
   const __amdgpu_buffer_rsrc_t dk_rsrc = make_rsrc(p.dk + kbase, k_rows * tok_bytes);
   const __amdgpu_buffer_rsrc_t dv_rsrc = make_rsrc(p.dv + kbase, k_rows * tok_bytes);
-  store_rows<D, BF16>(acc_k, p.scale, dk_rsrc, row_voff);
-  store_rows<D, BF16>(acc_v, 1.0f, dv_rsrc, row_voff);
+  if constexpr (DO_K) store_rows<D, BF16>(acc_k, p.scale, dk_rsrc, row_voff);
+  if constexpr (DO_V) store_rows<D, BF16>(acc_v, 1.0f, dv_rsrc, row_voff);
 }
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
@@ -569,8 +587,17 @@ hipError_t launch_one(BwdParams p, hipStream_t stream) {
                      dim3(NW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, stream, p);
+  if (D == 128 && SDPA_BWD_SPLIT_128) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN, DKDV_V>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN, DKDV_K>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN, DKDV_BOTH>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
