@@ -188,10 +188,11 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
  * REQUIRED here). dout, dq, dk, dv have q's layout and dtype; dq, dk, dv are
  * written (rounded to nearest even) and must not overlap the inputs.
  *   workspace : DEVICE memory of attn_bwd_workspace_size(B, H, S, packed)
- *               bytes (one fp32 per row and head), 16-byte aligned, owned by
+ *               bytes (two fp32 per row and head), 16-byte aligned, owned by
  *               the caller, used until the stream passes the call.
- * Two kernels run on `stream`: dq (which also fills the workspace with
- * rowsum(dout * out)), then dk and dv. No atomics: results are
+ * Kernels on `stream`: dq (which also fills the workspace with
+ * rowsum(dout * out) and lse * log2(e)), then dk and dv (two launches for
+ * D = 128, one for D = 64). No atomics: results are
  * deterministic. Errors as attn_fwd, plus ATTN_ERR_NULL for a missing lse,
  * dout, dq, dk or dv and ATTN_ERR_WORKSPACE.
  */

@@ -230,7 +230,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
 size_t attn_bwd_workspace_size(int B, int H, int S, int packed) {
   if (H < 1 || S < 0 || B < 0) return 0;
   const long long rows = packed ? (long long)S : (long long)B * S;
-  return (size_t)rows * H * sizeof(float);
+  return 2 * (size_t)rows * H * sizeof(float);   // rowsum(dO * O) and LSE * log2(e)
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -268,6 +268,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
   p.delta = static_cast<float*>(workspace);
+  p.lse2 = p.delta + need / (2 * sizeof(float));
   p.cu_seqlens = cu_seqlens;
   p.B = B;
   p.H = H;

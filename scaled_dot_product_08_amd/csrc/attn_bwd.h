@@ -17,6 +17,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* delta;               // workspace: rowsum(dO * O), same layout as lse
+  float* lse2;                // workspace: lse * log2(e), same layout
   const int32_t* cu_seqlens;  // packed mode offsets, or nullptr
   int B, H, S;
   int n_tiles;                // 128-row tiles per (sequence, head), set by the launcher

@@ -15,7 +15,7 @@
 //     delta for its rows and stores it for the second kernel.
 //   * dK/dV kernel: one workgroup per 128-key tile. Each wave keeps K^T and
 //     V^T of its 32 keys in registers and streams 64-row Q and dO tiles
-//     (with their LSE and delta) through the ring.
+//     (with their LSE, in log2 units, and delta) through the ring.
 // Orientation follows the forward: every MFMA's output column is the lane
 // (mod 32). In the dQ kernel the lane owns a query row, so LSE and delta
 // are one value per lane; in the dK/dV kernel the lane owns a key and the
@@ -292,7 +292,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
   const float delta = half_sum(dpart);
   const float lse2 = (qi < L) ? p.lse[row_base + qi] * LOG2E : 0.0f;
-  if (hh == 0 && qi < L) p.delta[row_base + qi] = delta;
+  if (hh == 0 && qi < L) {
+    // For the dK/dV kernel: delta, and the LSE in log2 units (saves a multiply per score there).
+    p.delta[row_base + qi] = delta;
+    p.lse2[row_base + qi] = lse2;
+  }
   const float c_log2 = p.c_log2;
 
   const O off(wave, lane, tok_bytes);
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) v
     if (wave == 0) {
       // 64 LSE and 64 delta values: lanes 0-15 fetch 16 bytes each, the
       // rest fall outside the descriptor and write zeros.
-      const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse + row_base + row0, rows * 4);
+      const __amdgpu_buffer_rsrc_t lr = make_rsrc(p.lse2 + row_base + row0, rows * 4);
       const __amdgpu_buffer_rsrc_t er = make_rsrc(p.delta + row_base + row0, rows * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (lds_void*)(stage + 2 * TILEB), 16, lane * 16, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (lds_void*)(stage + 2 * TILEB + 1024), 16, lane * 16, 0, 0, 0);
@@ -517,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) v
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[e] * LOG2E));
+          float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c_log2, -l4[e]));
           if (need_mask) {
             const int qrow = qb0 + 8 * g + 4 * hh + e;
             if (!(qrow < L && (!CAUSAL || qrow >= ki))) pr = 0.0f;

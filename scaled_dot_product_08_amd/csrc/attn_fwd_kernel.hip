@@ -538,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 // problem has enough 256-row tiles to fill the chip several times over; else
 // 4 waves (128 rows, two workgroups per CU), which balances small problems
 // better. Both share every per-row arithmetic step, so results are identical.
-constexpr long long kBigProblemTiles = 4096;
+constexpr long long kBigProblemTiles = 2048;
 
 static int choose_waves(const FwdParams& p, bool varlen) {
   // ATTN_WAVES=4 or 8 overrides the choice (used by tests to cover both).

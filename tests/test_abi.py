@@ -142,15 +142,15 @@ def call_bwd(**kw):
     (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
     (dict(dtype=7), -3), (dict(D=32), -5), (dict(scale=float("nan")), -4), (dict(H=0), -2),
     (dict(do=P + 8), -8), (dict(dv=P + 2), -8), (dict(lse=P + 1), -8),
-    (dict(), -9), (dict(ws=P, wsb=2 * 128 * 4 - 1), -9), (dict(ws=P + 4, wsb=1 << 20), -8),
+    (dict(), -9), (dict(ws=P, wsb=2 * 2 * 128 * 4 - 1), -9), (dict(ws=P + 4, wsb=1 << 20), -8),
 ])
 def test_bwd_argument_errors(kw, code):
     assert call_bwd(**kw) == code
 
 
 def test_bwd_workspace_and_empty(lib):
-    assert binding.bwd_workspace_size(2, 3, 100, False) == 2 * 3 * 100 * 4
-    assert binding.bwd_workspace_size(5, 3, 100, True) == 3 * 100 * 4
+    assert binding.bwd_workspace_size(2, 3, 100, False) == 2 * 2 * 3 * 100 * 4
+    assert binding.bwd_workspace_size(5, 3, 100, True) == 2 * 3 * 100 * 4
     assert call_bwd(S=0) == 0
     assert call_bwd(B=0, cu=P, S=10) == 0
 
