@@ -83,8 +83,10 @@ enum {
  * enqueued; ATTN_ERR_LAUNCH if the launch fails (hipGetLastError).
  *
  * Tuning: the library picks 128- or 256-row query tiles per workgroup from
- * the problem size; ATTN_WAVES=4 / ATTN_WAVES=8 forces 128 / 256 (results are
- * bitwise identical either way).
+ * the problem size; ATTN_WAVES=4 / ATTN_WAVES=8 forces 128 / 256 (for D = 128
+ * the results are bitwise identical either way; for D = 64 the 128-row
+ * kernel walks 128-key tiles instead of 64 and the results differ by
+ * rounding only).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int S, int D, int causal, float scale, int dtype,

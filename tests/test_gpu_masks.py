@@ -64,13 +64,17 @@ def test_ext_packed(window, n_global, alibi, causal):
 
 
 def test_ext_zero_slopes_match_plain():
+    """Zero ALiBi slopes change nothing beyond rounding. The plain D = 64 kernel
+    walks keys in 128-key tiles and the variant kernel in 64-key tiles, so the
+    fp16 row sums (of rounded probabilities, 2^-11 each) are grouped
+    differently; each LSE is within 2.5e-4 of exact, so they differ by <= 5e-4."""
     qb, kb, vb = synth.normal_qkv((1, 300, 2, 64), "fp16", 4200)
     q, k, v = (to_dev(x, "fp16") for x in (qb, kb, vb))
     o0, l0 = binding.fwd(q, k, v, causal=True)
     o1, l1 = binding.fwd(q, k, v, causal=True, alibi_slopes=torch.zeros(2, device="cuda"))
     torch.cuda.synchronize()
     assert (o0.float() - o1.float()).abs().max().item() <= 2e-3
-    assert (l0 - l1).abs().max().item() <= 1e-5
+    assert (l0 - l1).abs().max().item() <= 5e-4
 
 
 def test_window_one_returns_v_bitwise():

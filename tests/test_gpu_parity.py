@@ -174,8 +174,12 @@ def test_lse_optional():
 
 
 @pytest.mark.parametrize("name", ["llama", "mha_causal"])
-def test_tile_size_choice_is_bitwise_neutral(name, monkeypatch):
-    """128- and 256-row query tiles give bitwise identical O and LSE (same per-row arithmetic)."""
+def test_tile_size_choice(name, monkeypatch):
+    """128- and 256-row query tiles: bitwise identical O and LSE for D = 128 (same per-row
+    arithmetic over the same 64-key tiles). For D = 64 the 4-wave kernel walks 128-key tiles,
+    so the lazy maximum and the fp16 row sums are grouped differently: each result is within
+    the oracle tolerance, hence they differ by at most twice it (O) and by 5e-4 (LSE, twice the
+    2.5e-4 bound of the fp16 row sums)."""
     cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg, B=2 if cfg.B > 2 else cfg.B)
     outs = []
@@ -183,7 +187,11 @@ def test_tile_size_choice_is_bitwise_neutral(name, monkeypatch):
         monkeypatch.setenv("ATTN_WAVES", w)
         o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
         outs.append((o.cpu(), lse.cpu()))
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    if cfg.D == 128:
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    else:
+        assert (outs[0][0].float() - outs[1][0].float()).abs().max().item() <= 2 * TOL_O[cfg.dtype]
+        assert (outs[0][1] - outs[1][1]).abs().max().item() <= 5e-4
 
 
 def test_page_s2050_ragged_case():
