@@ -146,6 +146,37 @@ def torch_float32():
     return torch.float32
 
 
+def _check_tensors(names, tensors, shape=None, dtype=None):
+    """Same shape, dtype and GPU device, contiguous (the library reads raw pointers)."""
+    first = tensors[0]
+    shape = tuple(first.shape) if shape is None else tuple(shape)
+    dtype = first.dtype if dtype is None else dtype
+    for n, t in zip(names, tensors):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if t.device != first.device:
+            raise ValueError(f"{n} is on {t.device}, expected {first.device}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {shape}")
+        if t.dtype != dtype:
+            raise ValueError(f"{n} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+
+
+def _check_aux(lse, lse_shape, cu_seqlens, device):
+    import torch
+    if lse is not None:
+        if (lse.dtype != torch.float32 or tuple(lse.shape) != tuple(lse_shape)
+                or lse.device != device or not lse.is_contiguous()):
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)} "
+                             f"on {device}")
+    if cu_seqlens is not None:
+        if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1
+                or cu_seqlens.device != device):
+            raise ValueError(f"cu_seqlens must be a 1-D int32 tensor on {device}")
+
+
 def _stream_ptr(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -162,15 +193,19 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
     ``scale=None`` means 1/sqrt(D) rounded to float32. ``window``, ``n_global`` and
     ``alibi_slopes`` (float32 device tensor of H slopes) call attn_fwd_ext.
     """
-    for t in (q, k, v, out):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(("q", "k", "v", "out"), (q, k, v, out))
     if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("padded mode takes (B, S, H, D) tensors")
         B, S, H, D = q.shape
         cu_ptr = None
+        _check_aux(lse, (B, H, S), None, q.device)
     else:
+        if q.dim() != 3:
+            raise ValueError("packed mode takes (T, H, D) tensors")
         T, H, D = q.shape
         B, S = cu_seqlens.numel() - 1, T
+        _check_aux(lse, (H, T), cu_seqlens, q.device)
         cu_ptr = cu_seqlens.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -228,13 +263,16 @@ def attn_decode(q, k_cache, v_cache, out, lse=None, *, seqlens_k=None, causal: b
     decode_workspace_size(...) bytes (allocated here with torch when None).
     """
     import torch
-    for t in (q, k_cache, v_cache, out):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(("q", "out"), (q, out))
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q is (B, Sq, H, D) and the caches (B, H, S_max, D)")
     B, Sq, H, D = q.shape
     S_max = k_cache.shape[2]
-    if tuple(k_cache.shape) != (B, H, S_max, D) or tuple(v_cache.shape) != (B, H, S_max, D):
-        raise ValueError("k_cache and v_cache must be (B, H, S_max, D)")
+    _check_tensors(("k_cache", "v_cache"), (k_cache, v_cache), shape=(B, H, S_max, D),
+                   dtype=q.dtype)
+    if k_cache.device != q.device:
+        raise ValueError("the caches must be on q's device")
+    _check_aux(lse, (B, H, Sq), None, q.device)
     if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B
                                   or seqlens_k.device != q.device):
         raise ValueError("seqlens_k must be an int32 tensor of B lengths on q's device")
@@ -270,15 +308,18 @@ def attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, *, causal: bool, scale: float 
              cu_seqlens=None, workspace=None, stream=None) -> None:
     """Call attn_bwd on torch device tensors (layouts as attn_fwd; lse required)."""
     import torch
-    for t in (q, k, v, out, dout, dq, dk, dv):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    _check_tensors(("q", "k", "v", "out", "dout", "dq", "dk", "dv"),
+                   (q, k, v, out, dout, dq, dk, dv))
+    if lse is None:
+        raise ValueError("attn_bwd needs the forward's lse")
     if cu_seqlens is None:
         B, S, H, D = q.shape
         cu_ptr = None
+        _check_aux(lse, (B, H, S), None, q.device)
     else:
         T, H, D = q.shape
         B, S = cu_seqlens.numel() - 1, T
+        _check_aux(lse, (H, T), cu_seqlens, q.device)
         cu_ptr = cu_seqlens.data_ptr()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -308,9 +349,7 @@ def fwd_fp8(q8, k8, v8, *, causal: bool, scale: float | None = None, descale_q: 
             with_lse: bool = True, stream=None):
     """attn_fwd_fp8 on uint8 device tensors of E4M3 codes. Returns (O, LSE or None)."""
     import torch
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError("q8, k8, v8 must be contiguous uint8 tensors of E4M3 codes")
+    _check_tensors(("q8", "k8", "v8"), (q8, k8, v8), dtype=torch.uint8)
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     out = torch.empty(q8.shape, dtype=out_dtype, device=q8.device)
     if cu_seqlens is None:

@@ -175,3 +175,15 @@ def test_fp8_argument_errors(kw, code):
 
 def test_fp8_empty_problem_is_noop():
     assert call_fp8(S=0) == 0
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks shapes, dtypes and devices before any library call."""
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.attn_fwd(q, q, q, q, causal=False)
+    with pytest.raises(ValueError):
+        binding.fwd_fp8(q, q, q, causal=False)
+    with pytest.raises(ValueError):
+        binding.attn_decode(q, q, q, q)
