@@ -27,10 +27,13 @@
 //     ds_read_b64_tr_b16. Each lane owns one query row, so rescaling the
 //     accumulator is a per-lane scalar multiply.
 //
-// Exponentials use exp2 on logits pre-multiplied by scale*log2(e). The row
-// maximum is refreshed lazily: the stale maximum is kept until the new one
-// exceeds it by more than 8 (log2 units; probabilities are then at most 256,
-// and the same maximum enters numerator and denominator), which skips most
+// Exponentials use exp2 on logits pre-multiplied by scale*log2(e). After a
+// wave's first tile, a tile's exponentials are first taken against the
+// running maximum as it stands, without computing the tile's row maximum:
+// softmax does not depend on the constant subtracted, and a row sum within
+// OPT_LIMIT bounds every probability of the tile. Only when that bound fails
+// is the row maximum taken and refreshed, lazily: the stale maximum is kept
+// until the new one exceeds it by more than 8 (log2 units), which skips most
 // accumulator rescales.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,6 +64,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int HEAD_GROUP = 4; // heads whose query tiles are interleaved on one XCD
 constexpr int NXCD = 8;       // accelerator complex dies; workgroups go round-robin over them
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
+constexpr float OPT_LIMIT = 32768.0f;   // largest probability the optimistic pass accepts (fp16-safe)
 constexpr int BUF_FLAGS = 0x00020000;   // raw buffer descriptor word 3 (32-bit dwords)
 
 // 32x32x16 MFMA, fp32 accumulate; a/b carry eight 16-bit values each.
@@ -430,55 +434,72 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       }
     }
 
-    // Row maximum over this tile (16 + 16 values here, the rest in lane ^ 32).
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int kb = 1; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    }
-    mx = half_max(mx);
     // With ALiBi the scores are already log2-scaled.
     const bool prescaled = EXT && use_alibi;
-    const float mx2 = prescaled ? mx : ((mx == -INFINITY) ? -INFINITY : mx * c_log2);
-
-    // Lazy refresh of the running maximum.
-    const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      const float m_new = bump ? mx2 : m_run;
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-
-    // P = exp2(s * c - m), packed to 16 bit for P V.
+    const float c_mul = prescaled ? 1.0f : c_log2;
+    // P = exp2(s * c - m), packed to 16 bit for P V; returns this lane's half
+    // of the tile's row sum.
     // l: bf16 keeps 8 significant bits, so a row with few visible keys would
     // carry up to 2^-9 relative error into ln(l) if l summed the rounded
     // values; it sums the fp32 values instead. fp16 (11 bits) keeps that
     // error below 2.5e-4 and sums the rounded pairs with one dot2.
     uint32_t pk[NKB][8];
-    float tile_l = 0.0f;
-    // A row that has seen no visible key yet keeps m = -inf (its scores here
-    // are all -inf too): subtract 0 instead, which gives exp2(-inf) = 0.
-    const float m_sub = (EXT && m_run == -INFINITY) ? 0.0f : m_run;
-    const float c_mul = prescaled ? 1.0f : c_log2;
+    auto exps = [&](float m_sub) {
+      float tl = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_mul, -m_sub));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_mul, -m_sub));
-        pk[kb][t] = pack2<BF16>(e0, e1);
-        if constexpr (BF16) {
-          tile_l += e0 + e1;
-        } else {
-          tile_l = add_pair_f16(pk[kb][t], tile_l);
+        for (int t = 0; t < 8; ++t) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t], c_mul, -m_sub));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * t + 1], c_mul, -m_sub));
+          pk[kb][t] = pack2<BF16>(e0, e1);
+          if constexpr (BF16) {
+            tl += e0 + e1;
+          } else {
+            tl = add_pair_f16(pk[kb][t], tl);
+          }
         }
       }
+      return tl;
+    };
+
+    // Optimistic pass: exponentials against the running maximum as it stands,
+    // with no row maximum of the tile at all. Every probability is at most
+    // the row sum, so a sum within OPT_LIMIT proves that none exceeded it
+    // (and none overflowed); only otherwise (or on a wave's first tile) is the
+    // maximum taken, refreshed and the exponentials redone. Softmax does not
+    // depend on which constant is subtracted, so this changes rounding only.
+    float tile_l = 0.0f;
+    bool redo = true;
+    if (j != j_lo) {
+      tile_l = exps(m_run);
+      redo = __builtin_amdgcn_ballot_w64(!(tile_l <= OPT_LIMIT)) != 0;
+    }
+    if (redo) {
+      // Row maximum over this tile (16 + 16 values here, the rest in lane ^ 32).
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      mx = half_max(mx);
+      const float mx2 = prescaled ? mx : ((mx == -INFINITY) ? -INFINITY : mx * c_log2);
+      // Lazy refresh of the running maximum.
+      const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
+      if (__builtin_amdgcn_ballot_w64(bump)) {
+        const float m_new = bump ? mx2 : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      // A row that has seen no visible key yet keeps m = -inf (its scores here
+      // are all -inf too): subtract 0 instead, which gives exp2(-inf) = 0.
+      tile_l = exps((EXT && m_run == -INFINITY) ? 0.0f : m_run);
     }
     l_run += tile_l;
 

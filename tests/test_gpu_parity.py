@@ -199,3 +199,36 @@ def test_page_s2050_ragged_case():
     qb, kb, vb = synth.normal_qkv((1, 2050, 2, 64), "fp16", 2050)
     check_full(qb, kb, vb, "fp16", False, scale_of(64))
     check_full(qb, kb, vb, "fp16", True, scale_of(64))
+
+
+def _ramp_qkv(B, S, H, D, dtype, step, seed, jump_every=0):
+    """Scores that climb along the key axis: every key row is (base + step * j) * u
+    for one unit direction u shared with the queries, plus small noise; with
+    jump_every > 0 the climb happens in steps at every jump_every-th key instead.
+    Later key tiles then exceed any maximum taken on earlier ones, which drives
+    the kernel's maximum refresh (and, for small steps, its acceptance of a stale
+    maximum) on every tile."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    j = np.arange(S, dtype=np.float64)
+    if jump_every:
+        j = np.floor(j / jump_every) * jump_every
+    q = np.broadcast_to(u, (B, S, H, D)) * 2.0 + 0.1 * rng.standard_normal((B, S, H, D))
+    k = (1.0 + step * j)[None, :, None, None] * u + 0.1 * rng.standard_normal((B, S, H, D))
+    v = rng.standard_normal((B, S, H, D))
+    return tuple(synth.to_bits(x.astype(np.float32), dtype) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("step,jump", [(0.05, 0), (0.12, 32), (0.4, 64), (1.0, 64)])
+def test_climbing_scores_refresh_the_maximum(dtype, D, causal, step, jump):
+    """Keys whose scores keep rising (linearly, or in jumps at tile and half-tile
+    boundaries): the running maximum is stale on almost every tile, by amounts
+    both below and far above the refresh thresholds. O and LSE stay within the
+    oracle tolerance."""
+    S = 333
+    qb, kb, vb = _ramp_qkv(1, S, 2, D, dtype, step, seed=91 + D + int(100 * step), jump_every=jump)
+    say(f"climb dtype={dtype} D={D} causal={causal} step={step} jump={jump}")
+    check_full(qb, kb, vb, dtype, causal, scale_of(D))
