@@ -27,7 +27,10 @@
 // P is quantised to E4M3 after scaling by 2^4 (probabilities relative to
 // the lazily refreshed maximum stay below 2^4, so P * 2^4 < 2^8 < 448, and
 // values down to 2^-13 of the maximum keep a code); the same factor is in
-// the row sum, so it cancels in O and is taken out of the LSE.
+// the row sum, so it cancels in O and is taken out of the LSE. After the
+// first tile the exponentials are first taken against the running maximum
+// without a row maximum; they are kept when the lane's row sum (a bound on
+// every P * 2^4) is at most 448.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,6 +63,7 @@ constexpr int DB = D / 32;        // 32-column blocks of O^T
 constexpr int HEAD_GROUP = 4;
 constexpr int NXCD = 8;
 constexpr float LAZY_RESCALE_LOG2 = 4.0f;
+constexpr float E4M3_MAX = 448.0f;       // largest finite E4M3 value
 constexpr float P_SHIFT_LOG2 = 4.0f;   // P is quantised as P * 2^4
 constexpr int BUF_FLAGS = 0x00020000;
 constexpr int E8M0_ONE = 127;          // block scale 2^0
@@ -268,39 +272,55 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
       }
     }
 
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = half_max(mx);
-    const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
-    const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
-    if (__builtin_amdgcn_ballot_w64(bump)) {
-      const float m_new = bump ? mx2 : m_run;
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-
     // P * 2^4 = exp2(s c - m + 4): E4M3 bytes for P V, fp32 for the row sum.
-    const float m_sub = m_run - P_SHIFT_LOG2;
     uint32_t pk[8];
-    float tile_l = 0.0f;
+    auto exps = [&](float m) {
+      const float m_sub = m - P_SHIFT_LOG2;
+      float tl = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, r0 = 4 * (w & 3);
-      float e[4];
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = 4 * (w & 3);
+        float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c_log2, -m_sub));
-        tile_l += e[i];
+        for (int i = 0; i < 4; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c_log2, -m_sub));
+          tl += e[i];
+        }
+        uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], (int)x, true);
+        pk[w] = x;
       }
-      uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
-      x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], (int)x, true);
-      pk[w] = x;
+      return tl;
+    };
+    // Optimistic pass (as in the 16-bit kernel): exponentials against the
+    // running maximum as it stands; a lane sum within E4M3_MAX bounds every
+    // scaled probability of the tile, so each keeps an exact-range code.
+    // Otherwise (or on the first tile) the row maximum is taken, refreshed
+    // lazily and the exponentials redone.
+    float tile_l = 0.0f;
+    bool redo = true;
+    if (j != 0) {
+      tile_l = exps(m_run);
+      redo = __builtin_amdgcn_ballot_w64(!(tile_l <= E4M3_MAX)) != 0;
+    }
+    if (redo) {
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      mx = half_max(mx);
+      const float mx2 = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
+      const bool bump = mx2 > m_run + LAZY_RESCALE_LOG2;
+      if (__builtin_amdgcn_ballot_w64(bump)) {
+        const float m_new = bump ? mx2 : m_run;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) acc[d] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      tile_l = exps(m_run);
     }
     l_run += tile_l;
 

@@ -17,7 +17,7 @@ import torch
 
 import synth
 from gpu_util import TOL_LSE, max_abs, say, scale_of, to_f64
-from oracle import attention_fp8, e4m3_decode
+from oracle import attention_fp8, e4m3_decode, e4m3_encode
 from oracle.attention import _head_rows, visible_mask
 from scaled_dot_product_08_amd import binding
 
@@ -121,3 +121,25 @@ def test_fp8_llama_shape_sampled():
         worst_l = max(worst_l, max_abs(lse[b, h, rows].numpy(), lref))
     say(f"    sampled max err/bound={worst:.3f} max|dLSE|={worst_l:.3e}")
     assert worst <= 1.0 and worst_l <= TOL_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("step,jump", [(0.02, 0), (0.1, 32), (0.08, 64)])
+def test_fp8_climbing_scores(step, jump, causal):
+    """Key scores that climb along the keys (linearly, or in jumps at 32- and 64-key
+    boundaries): the running maximum is stale on almost every tile, by amounts below
+    and far above what the kernel accepts without a refresh (every P * 2^4 must stay
+    within the E4M3 range). Same bound as the other cases."""
+    S, H, D = 333, 2, 128
+    rng = np.random.default_rng(7300 + int(100 * step) + jump)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    j = np.arange(S, dtype=np.float64)
+    if jump:
+        j = np.floor(j / jump) * jump
+    q = np.broadcast_to(u, (1, S, H, D)) * 4.0 + 0.1 * rng.standard_normal((1, S, H, D))
+    k = (1.0 + step * j)[None, :, None, None] * u * 4.0 + 0.1 * rng.standard_normal((1, S, H, D))
+    v = rng.standard_normal((1, S, H, D))
+    q8, k8, v8 = (e4m3_encode(x) for x in (q, k, v))
+    say(f"fp8 climbing step={step} jump={jump} causal={causal}")
+    check(q8, k8, v8, causal, scale_of(D), (1.0, 1.0, 1.0), "bf16")
