@@ -40,6 +40,12 @@
 
 #include <cstdlib>
 
+#ifndef SDPA_W64_ASM
+#define SDPA_W64_ASM 1
+#endif
+#ifndef SDPA_W64_OVERLAP
+#define SDPA_W64_OVERLAP 1
+#endif
 #ifndef SDPA_SCHED_QK
 #define SDPA_SCHED_QK 1
 #endif
@@ -77,6 +83,34 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
+}
+
+// The same MFMA with the accumulator held in the accumulation registers
+// (AGPRs), for kernels whose accumulators do not fit beside the working set in
+// the 256 VGPRs. Written as assembly because the compiler otherwise places
+// every MFMA result of such a kernel in AGPRs, scores included. The compiler's
+// hazard model does not see these instructions; callers keep the rules:
+// an operand written by a VALU instruction is at least 2 wait states old
+// (operand_fence), and the accumulators are read or written by anything but
+// these MFMAs only across acc_fence.
+template <bool BF16>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, u32x4 a, u32x4 b) {
+  if constexpr (BF16) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  } else {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  }
+}
+// 16 wait states between the last MFMA writing or reading an accumulator and
+// a VALU access to it (gfx950 needs 12 after an 8-pass XDL write), and more
+// than the 2 that a VALU write needs before an MFMA reads it.
+__device__ __forceinline__ void acc_fence(f32x16& a) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(a));
+}
+// 2 wait states after VALU writes of MFMA operands (the probabilities, packed
+// by VALU instructions), applied to the assembled operand registers.
+__device__ __forceinline__ void operand_fence(u32x4& a, u32x4& b) {
+  asm volatile("s_nop 1" : "+v"(a), "+v"(b));
 }
 
 // Two floats -> two 16-bit values (round to nearest even), low half first.
@@ -565,6 +599,424 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-block waves: 64 query rows per wave (two 32-row blocks), 4 waves and 256
+// rows per workgroup, one wave per SIMD. Every K and V^T operand a wave reads
+// from LDS feeds two MFMAs, one per row block, so LDS read traffic per matrix
+// operation is half that of the 32-row waves above (whose eight waves per CU
+// read 256 KB of K and V per 64-key tile, about what LDS delivers in the time
+// the matrix cores take for the tile). With 512 registers per lane available
+// at one wave per SIMD, the 2*D/32 output accumulators sit in the
+// accumulation registers. Inside a tile the two 32-key blocks form a short
+// software pipeline that a single wave can overlap on its own: the
+// exponentials of key block 0 are independent of the scores of block 1, and
+// those of block 1 of P V over block 0. The per-row arithmetic (optimistic
+// exponentials, lazy maximum, row sums) is that of the 32-row kernel, applied
+// per 32-key block instead of per 64-key tile.
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
+  constexpr int NWAVES = 4;
+  constexpr int BM = 256;                      // query rows per workgroup
+  constexpr int BN = 64;                       // keys per LDS tile
+  constexpr int NKB = 2;                       // 32-key blocks per tile
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BN * ROWB;
+  constexpr int STAGEB = 2 * TILEB;
+  constexpr int LDW = TILEB / 1024 / NWAVES;
+  constexpr int DCH = D / 16;
+  constexpr int DB = D / 32;
+  static_assert(LDW >= 1, "tile must give every wave a 1 KB load");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int li = lane & 31;
+  const int hh = lane >> 5;
+
+  // Same XCD-aware order as the 32-row kernel: contiguous runs of the logical
+  // order per XCD, heads in groups of HEAD_GROUP, longest tiles first.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % NXCD;
+  const int local = blockIdx.x / NXCD;
+  const int gq = G / NXCD, gr = G % NXCD;
+  const int logical = (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
+  const int nbh = VARLEN ? p.H : p.B * p.H;
+  const int nt = p.n_qtiles;
+  const int grp = logical / (HEAD_GROUP * nt);
+  const int in_grp = min(HEAD_GROUP, nbh - grp * HEAD_GROUP);
+  const int rem = logical - grp * (HEAD_GROUP * nt);
+  const int rank = rem / in_grp;
+  const int bh = grp * HEAD_GROUP + (rem - rank * in_grp);
+  const int h = bh % p.H;
+  const int b = VARLEN ? 0 : bh / p.H;
+  const int vt = nt - 1 - rank;
+  int seq_start = 0, L = p.S, q0;
+  if constexpr (VARLEN) {
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_seqlens[mid] / BM + mid <= vt) lo = mid; else hi = mid - 1;
+    }
+    seq_start = p.cu_seqlens[lo];
+    L = p.cu_seqlens[lo + 1] - seq_start;
+    q0 = (vt - (seq_start / BM + lo)) * BM;
+    if (q0 >= L) return;
+  } else {
+    q0 = vt * BM;
+  }
+
+  const uint32_t tok_bytes = (uint32_t)p.H * ROWB;
+  const size_t base = (((size_t)b * p.S + seq_start) * p.H + h) * D;
+  const uint16_t* qg = p.q + base + (size_t)q0 * p.H * D;
+  const uint16_t* kg = p.k + base;
+  const uint16_t* vg = p.v + base;
+  uint16_t* og = p.o + base + (size_t)q0 * p.H * D;
+
+  const int kv_hi = CAUSAL ? min(q0 + BM, L) : L;
+  const int n_kv = (kv_hi + BN - 1) / BN;
+  const int wq0 = q0 + wave * 64;               // first query row of this wave
+  const uint32_t q_rows = (uint32_t)min(L - q0, BM);
+
+  // Q^T operands of both row blocks, resident for the whole key loop.
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qg, q_rows * tok_bytes);
+  const uint32_t q_xor = (p.q_mode == 1) ? 0x80008000u : 0u;
+  const uint32_t q_and = (p.q_mode == 2) ? 0u : 0xffffffffu;
+  u32x4 qreg[2][DCH];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint32_t q_voff = (uint32_t)(wave * 64 + rb * 32 + li) * tok_bytes + hh * 16;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      qreg[rb][c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_voff + c * 32, 0, 0));
+      qreg[rb][c] = (qreg[rb][c] ^ q_xor) & q_and;
+    }
+  }
+  const float c_log2 = p.c_log2;
+
+  uint32_t ld_voff[LDW];
+#pragma unroll
+  for (int u = 0; u < LDW; ++u) {
+    const int byte = (wave * LDW + u) * 1024 + lane * 16;
+    const int r = byte / ROWB, pc = (byte % ROWB) / 16;
+    ld_voff[u] = (uint32_t)r * tok_bytes + (uint32_t)((pc ^ swz<D>(r)) * 16);
+  }
+  uint32_t k_off[DCH];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) k_off[c] = li * ROWB + (((2 * c + hh) ^ swz<D>(li)) << 4);
+  uint32_t v_off[2][DB];
+  {
+    const int blk = li >> 4, s = li & 15;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int key = t2 * 8 + hh * 4 + (s >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int col = db * 32 + blk * 16 + swap23(4 * (s & 3));
+        v_off[t2][db] = key * ROWB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) * 2));
+      }
+    }
+  }
+
+  auto issue_tile = [&](int j, int st) __attribute__((always_inline)) {
+    const int key0 = j * BN;
+    const uint32_t rows = (uint32_t)min(L - key0, BN);
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
+    uint8_t* kdst = (st ? smem1 : smem0) + wave * LDW * 1024;
+    uint8_t* vdst = kdst + TILEB;
+#pragma unroll
+    for (int u = 0; u < LDW; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < LDW; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[2][DB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      acc[rb][d] = f32x16{};
+      acc_fence(acc[rb][d]);
+    }
+  }
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.0f, 0.0f};
+
+  // S^T of one 32-key block for both row blocks: each K operand feeds two
+  // MFMAs; the two chains alternate and K is read two steps ahead.
+  auto qk_block = [&](const uint8_t* ks, int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    auto kread = [&](int c) __attribute__((always_inline)) { return *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]); };
+    u32x4 ka[2] = {kread(0), kread(1)};
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      s[0] = mfma32<BF16>(ka[c & 1], qreg[0][c], s[0]);
+      s[1] = mfma32<BF16>(ka[c & 1], qreg[1][c], s[1]);
+      if (c + 2 < DCH) ka[c & 1] = kread(c + 2);
+    }
+  };
+  auto mask_block = [&](int key0, int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int qi = wq0 + rb * 32 + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        const bool ok = (key < L) && (!CAUSAL || key <= qi);
+        s[rb][r] = ok ? s[rb][r] : -INFINITY;
+      }
+    }
+  };
+  // P = exp2(s * c - m) of one row block and key block, packed to 16 bit;
+  // returns this lane's half of the block's row sum (fp32 sums for bf16, one
+  // dot2 per rounded pair for fp16, as in the 32-row kernel).
+  auto exps = [&](const f32x16& s, uint32_t (&pk)[8], float m_sub) __attribute__((always_inline)) {
+    float tl = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * t], c_log2, -m_sub));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * t + 1], c_log2, -m_sub));
+      pk[t] = pack2<BF16>(e0, e1);
+      if constexpr (BF16) {
+        tl += e0 + e1;
+      } else {
+        tl = add_pair_f16(pk[t], tl);
+      }
+    }
+    return tl;
+  };
+  // Accept the optimistic exponentials of a key block, or take the row
+  // maximum, refresh the running maximum lazily and redo them. A wave's first
+  // block always lands here (m = -inf makes the optimistic sums inf or NaN).
+  auto settle = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], float (&tl)[2]) __attribute__((always_inline)) {
+    const bool bad = !(tl[0] <= OPT_LIMIT) || !(tl[1] <= OPT_LIMIT);
+    if (__builtin_amdgcn_ballot_w64(bad)) {
+      float mx2[2];
+      bool bump[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float mx = s[rb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
+        mx = half_max(mx);
+        mx2[rb] = (mx == -INFINITY) ? -INFINITY : mx * c_log2;
+        bump[rb] = mx2[rb] > m_run[rb] + LAZY_RESCALE_LOG2;
+      }
+      if (__builtin_amdgcn_ballot_w64(bump[0] || bump[1])) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const float m_new = bump[rb] ? mx2[rb] : m_run[rb];
+          const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            acc_fence(acc[rb][d]);
+            acc[rb][d] *= alpha;
+            acc_fence(acc[rb][d]);
+          }
+          l_run[rb] *= alpha;
+          m_run[rb] = m_new;
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) tl[rb] = exps(s[rb], pk[rb], (m_run[rb] == -INFINITY) ? 0.0f : m_run[rb]);
+    }
+    l_run[0] += tl[0];
+    l_run[1] += tl[1];
+  };
+  // The B operands (probabilities) of one key block: [16-key step][row block].
+  auto p_operands = [&](const uint32_t (&pk)[2][8], u32x4 (&bo)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        bo[e][rb] = u32x4{pk[rb][e * 4 + 0], pk[rb][e * 4 + 1], pk[rb][e * 4 + 2], pk[rb][e * 4 + 3]};
+      }
+    }
+    operand_fence(bo[0][0], bo[0][1]);
+    operand_fence(bo[1][0], bo[1][1]);
+  };
+  // O^T += V^T P^T over the two 16-key steps of key block kb; every V^T
+  // operand feeds both row blocks.
+  auto pv_block = [&](const uint8_t* vs, int kb, const uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    u32x4 bo[2][2];
+    p_operands(pk, bo);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const u32x4 b0 = bo[e][0], b1 = bo[e][1];
+      const uint8_t* vb = vs + (kb * 2 + e) * 16 * ROWB;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+#if SDPA_W64_ASM
+        mfma32_acc<BF16>(acc[0][d], a, b0);
+        mfma32_acc<BF16>(acc[1][d], a, b1);
+#else
+        acc[0][d] = mfma32<BF16>(a, b0, acc[0][d]);
+        acc[1][d] = mfma32<BF16>(a, b1, acc[1][d]);
+#endif
+      }
+    }
+  };
+
+  // P V over key block 0 interleaved by hand with the exponentials of key
+  // block 1 (the accumulator MFMAs are assembly, which the compiler does not
+  // schedule): after every MFMA, 4/DB pairs of exponentials, with scheduling
+  // fences in between; the V^T operands are read two steps ahead.
+  auto pv0_with_exps1 = [&](const uint8_t* vs, const uint32_t (&pkA)[2][8], const f32x16 (&s)[2],
+                            uint32_t (&pkB)[2][8], float (&tl)[2]) __attribute__((always_inline)) {
+    constexpr int NSTEP = 2 * DB;                 // (16-key step, 32-column block) pairs
+    constexpr int PAIRS_PER_MFMA = 16 / (2 * NSTEP);
+    auto vread = [&](int st) __attribute__((always_inline)) {
+      const int e = st / DB, d = st % DB;
+      const uint8_t* vb = vs + e * 16 * ROWB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    float m_neg[2] = {-m_run[0], -m_run[1]};
+    tl[0] = 0.0f;
+    tl[1] = 0.0f;
+    auto exp_pairs = [&](int first) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < PAIRS_PER_MFMA; ++q) {
+        const int pr = first + q, rb = pr / 8, t = pr % 8;
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * t], c_log2, m_neg[rb]));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * t + 1], c_log2, m_neg[rb]));
+        pkB[rb][t] = pack2<BF16>(e0, e1);
+        if constexpr (BF16) {
+          tl[rb] += e0 + e1;
+        } else {
+          tl[rb] = add_pair_f16(pkB[rb][t], tl[rb]);
+        }
+      }
+    };
+    u32x4 bo[2][2];
+    p_operands(pkA, bo);
+    u32x4 va[3];
+    va[0] = vread(0);
+    va[1] = vread(1);
+    int pr = 0;
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + 2 < NSTEP) va[(st + 2) % 3] = vread(st + 2);
+      const int e = st / DB, d = st % DB;
+      const u32x4 b0 = bo[e][0], b1 = bo[e][1];
+      __builtin_amdgcn_sched_barrier(0);
+#if SDPA_W64_ASM
+      mfma32_acc<BF16>(acc[0][d], va[st % 3], b0);
+#else
+      acc[0][d] = mfma32<BF16>(va[st % 3], b0, acc[0][d]);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      exp_pairs(pr);
+      pr += PAIRS_PER_MFMA;
+      __builtin_amdgcn_sched_barrier(0);
+#if SDPA_W64_ASM
+      mfma32_acc<BF16>(acc[1][d], va[st % 3], b1);
+#else
+      acc[1][d] = mfma32<BF16>(va[st % 3], b1, acc[1][d]);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      exp_pairs(pr);
+      pr += PAIRS_PER_MFMA;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One body for masked and unmasked tiles (the masks are small conditional
+  // regions): two specialised copies of the tile would meet at a join where
+  // the allocator moves the accumulators between registers.
+  auto compute_tile = [&](int j, const uint8_t* ks, bool need_mask) __attribute__((always_inline)) {
+    const uint8_t* vs = ks + TILEB;
+    const int key0 = j * BN;
+    f32x16 s0[2], s1[2];
+    uint32_t pk0[2][8], pk1[2][8];
+    float tl0[2], tl1[2];
+    qk_block(ks, 0, s0);
+    if (need_mask) mask_block(key0, 0, s0);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) tl0[rb] = exps(s0[rb], pk0[rb], m_run[rb]);
+    qk_block(ks, 1, s1);
+    if (need_mask) mask_block(key0, 1, s1);
+    settle(s0, pk0, tl0);
+#if SDPA_W64_OVERLAP
+    pv0_with_exps1(vs, pk0, s1, pk1, tl1);
+#else
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) tl1[rb] = exps(s1[rb], pk1[rb], m_run[rb]);
+    pv_block(vs, 0, pk0);
+#endif
+    settle(s1, pk1, tl1);
+    pv_block(vs, 1, pk1);
+  };
+  auto tile = [&](int j, const uint8_t* ks) __attribute__((always_inline)) {
+    const int key0 = j * BN;
+    if (CAUSAL && key0 > wq0 + 63) return;      // no row of this wave sees the tile
+    compute_tile(j, ks, (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0));
+  };
+
+  // Pairs of tiles, then an odd last tile after the loop: no exit in the
+  // middle of the loop body, so the accumulators keep one register assignment
+  // through both halves (a mid-body exit made the allocator copy them at the
+  // join, which would read assembly-MFMA results without wait states).
+  issue_tile(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+  int j = 0;
+#pragma unroll 1
+  for (; j + 1 < n_kv; j += 2) {
+    issue_tile(j + 1, 1);
+    tile(j, smem0);
+    wait_vmem_all();
+    __syncthreads();
+    if (j + 2 < n_kv) issue_tile(j + 2, 0);
+    tile(j + 1, smem1);
+    wait_vmem_all();
+    __syncthreads();
+  }
+  if (j < n_kv) tile(j, smem0);
+
+  const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(og, q_rows * tok_bytes);
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) acc_fence(acc[rb][d]);
+    const float l_tot = half_sum(l_run[rb]);
+    const float inv = 1.0f / l_tot;
+    const uint32_t o_voff = (uint32_t)(wave * 64 + rb * 32 + li) * tok_bytes + hh * 16;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w[t] = pack2<BF16>(acc[rb][d][half * 8 + 2 * t] * inv, acc[rb][d][half * 8 + 2 * t + 1] * inv);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), o_rsrc,
+                                               o_voff + (uint32_t)(d * 64 + half * 32), 0, 0);
+      }
+    }
+    const int qi = wq0 + rb * 32 + li;
+    if (p.lse != nullptr && hh == 0 && qi < L) {
+      const float lse = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+      p.lse[((size_t)b * p.H + h) * p.S + seq_start + qi] = lse;
+    }
+  }
+}
+
 // Workgroup size: 8 waves (256 query rows, one workgroup per CU) when the
 // problem has enough 256-row tiles to fill the chip several times over; else
 // 4 waves (128 rows, two workgroups per CU), which balances small problems
@@ -576,6 +1028,7 @@ static int choose_waves(const FwdParams& p, bool varlen) {
   if (const char* e = std::getenv("ATTN_WAVES")) {
     if (e[0] == '4' && e[1] == '\0') return 4;
     if (e[0] == '8' && e[1] == '\0') return 8;
+    if (e[0] == 'w' && e[1] == '6' && e[2] == '4' && e[3] == '\0') return 64;
   }
   const long long bh = varlen ? p.H : (long long)p.B * p.H;
   const long long tiles256 = varlen ? (long long)p.S / 256 + p.B : ((long long)p.S + 255) / 256;
@@ -597,13 +1050,26 @@ static hipError_t launch_one(FwdParams p, hipStream_t stream) {
 }
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+static hipError_t launch_w64(FwdParams p, hipStream_t stream) {
+  constexpr long long BM = 256;
+  const long long tiles = VARLEN ? (long long)p.S / BM + p.B : ((long long)p.S + BM - 1) / BM;
+  p.n_qtiles = (int)tiles;
+  const long long grid = tiles * (VARLEN ? p.H : (long long)p.B * p.H);
+  hipLaunchKernelGGL((attn_fwd_w64_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 static hipError_t launch_nw(const FwdParams& p, hipStream_t stream) {
   // The mask/bias variants run with 4-wave workgroups only.
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
     return launch_one<D, BF16, CAUSAL, VARLEN, 4, true>(p, stream);
   }
-  return choose_waves(p, VARLEN) == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, stream)
-                                      : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, stream);
+  const int w = choose_waves(p, VARLEN);
+  if (w == 64) return launch_w64<D, BF16, CAUSAL, VARLEN>(p, stream);
+  return w == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, stream)
+                : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, stream);
 }
 
 template <int D, bool BF16>

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
-@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("waves", ["4", "8", "w64"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
@@ -74,7 +74,7 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("waves", ["4", "8", "w64"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_guard_bands_untouched(packed, waves, monkeypatch):
     """Sentinel regions around out and lse stay intact (no writes past the tensors)."""

@@ -128,11 +128,12 @@ SHAPES = [
 ]
 
 
-@pytest.fixture(params=["4", "8"], ids=["bm128", "bm256"])
+@pytest.fixture(params=["4", "8", "w64"], ids=["bm128", "bm256", "bm256w64"])
 def waves(request, monkeypatch):
-    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles."""
+    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles, and with the
+    256-row tiles of four 64-row waves."""
     monkeypatch.setenv("ATTN_WAVES", request.param)
-    return int(request.param)
+    return request.param
 
 
 @pytest.mark.parametrize("D", [64, 128])
