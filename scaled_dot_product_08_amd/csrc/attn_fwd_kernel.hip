@@ -35,17 +35,20 @@
 // is the row maximum taken and refreshed, lazily: the stale maximum is kept
 // until the new one exceeds it by more than 8 (log2 units), which skips most
 // accumulator rescales.
+//
+// A second kernel (attn_fwd_w64_kernel, below) gives each wave 64 query rows
+// so that every K and V^T operand read from LDS feeds two MFMAs, runs one wave
+// per SIMD with the output accumulators in AGPRs (their MFMAs are inline
+// assembly, guarded by explicit wait states that the build verifies on the
+// emitted code), and software-pipelines the 32-key blocks of a three-stage LDS
+// ring so that every group of MFMAs has softmax work beside it. It is the
+// default for D = 64 without causality.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <cstdlib>
+#include <type_traits>
 
-#ifndef SDPA_W64_ASM
-#define SDPA_W64_ASM 1
-#endif
-#ifndef SDPA_W64_OVERLAP
-#define SDPA_W64_OVERLAP 1
-#endif
 #ifndef SDPA_SCHED_QK
 #define SDPA_SCHED_QK 1
 #endif
@@ -618,7 +621,6 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
   constexpr int NWAVES = 4;
   constexpr int BM = 256;                      // query rows per workgroup
   constexpr int BN = 64;                       // keys per LDS tile
-  constexpr int NKB = 2;                       // 32-key blocks per tile
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BN * ROWB;
   constexpr int STAGEB = 2 * TILEB;
@@ -629,6 +631,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -725,7 +728,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
     const uint32_t rows = (uint32_t)min(L - key0, BN);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
-    uint8_t* kdst = (st ? smem1 : smem0) + wave * LDW * 1024;
+    uint8_t* kdst = (st == 0 ? smem0 : (st == 1 ? smem1 : smem2)) + wave * LDW * 1024;
     uint8_t* vdst = kdst + TILEB;
 #pragma unroll
     for (int u = 0; u < LDW; ++u) {
@@ -755,12 +758,15 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
     s[0] = f32x16{};
     s[1] = f32x16{};
     auto kread = [&](int c) __attribute__((always_inline)) { return *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]); };
-    u32x4 ka[2] = {kread(0), kread(1)};
+    constexpr int KP = 2;                         // K operands read ahead
+    u32x4 ka[KP];
+#pragma unroll
+    for (int c = 0; c < KP; ++c) ka[c] = kread(c);
 #pragma unroll
     for (int c = 0; c < DCH; ++c) {
-      s[0] = mfma32<BF16>(ka[c & 1], qreg[0][c], s[0]);
-      s[1] = mfma32<BF16>(ka[c & 1], qreg[1][c], s[1]);
-      if (c + 2 < DCH) ka[c & 1] = kread(c + 2);
+      s[0] = mfma32<BF16>(ka[c % KP], qreg[0][c], s[0]);
+      s[1] = mfma32<BF16>(ka[c % KP], qreg[1][c], s[1]);
+      if (c + KP < DCH) ka[c % KP] = kread(c + KP);
     }
   };
   auto mask_block = [&](int key0, int kb, f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -843,150 +849,129 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
     operand_fence(bo[0][0], bo[0][1]);
     operand_fence(bo[1][0], bo[1][1]);
   };
-  // O^T += V^T P^T over the two 16-key steps of key block kb; every V^T
-  // operand feeds both row blocks.
-  auto pv_block = [&](const uint8_t* vs, int kb, const uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
-    u32x4 bo[2][2];
-    p_operands(pk, bo);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const u32x4 b0 = bo[e][0], b1 = bo[e][1];
-      const uint8_t* vb = vs + (kb * 2 + e) * 16 * ROWB;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-#if SDPA_W64_ASM
-        mfma32_acc<BF16>(acc[0][d], a, b0);
-        mfma32_acc<BF16>(acc[1][d], a, b1);
-#else
-        acc[0][d] = mfma32<BF16>(a, b0, acc[0][d]);
-        acc[1][d] = mfma32<BF16>(a, b1, acc[1][d]);
-#endif
-      }
-    }
-  };
-
-  // P V over key block 0 interleaved by hand with the exponentials of key
-  // block 1 (the accumulator MFMAs are assembly, which the compiler does not
-  // schedule): after every MFMA, 4/DB pairs of exponentials, with scheduling
-  // fences in between; the V^T operands are read two steps ahead.
-  auto pv0_with_exps1 = [&](const uint8_t* vs, const uint32_t (&pkA)[2][8], const f32x16 (&s)[2],
-                            uint32_t (&pkB)[2][8], float (&tl)[2]) __attribute__((always_inline)) {
+  // P V over key block kb of the stage at vs (both row blocks, 2*2*DB MFMAs),
+  // interleaved by hand with the exponentials of one row block of another key
+  // block (8 pairs, spread evenly over the MFMAs). The accumulator MFMAs are
+  // assembly, which the compiler does not schedule, hence the fences; the V^T
+  // operands are read two steps ahead.
+  auto pv_with_exps = [&](const uint8_t* vs, int kb, const uint32_t (&pkA)[2][8], const f32x16& s,
+                          uint32_t (&pkB)[8], float& tl, float m_sub) __attribute__((always_inline)) {
     constexpr int NSTEP = 2 * DB;                 // (16-key step, 32-column block) pairs
-    constexpr int PAIRS_PER_MFMA = 16 / (2 * NSTEP);
+    constexpr int NM = 2 * NSTEP;                 // MFMAs
     auto vread = [&](int st) __attribute__((always_inline)) {
       const int e = st / DB, d = st % DB;
-      const uint8_t* vb = vs + e * 16 * ROWB;
+      const uint8_t* vb = vs + (kb * 2 + e) * 16 * ROWB;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
       const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
       return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     };
-    float m_neg[2] = {-m_run[0], -m_run[1]};
-    tl[0] = 0.0f;
-    tl[1] = 0.0f;
-    auto exp_pairs = [&](int first) __attribute__((always_inline)) {
-#pragma unroll
-      for (int q = 0; q < PAIRS_PER_MFMA; ++q) {
-        const int pr = first + q, rb = pr / 8, t = pr % 8;
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * t], c_log2, m_neg[rb]));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[rb][2 * t + 1], c_log2, m_neg[rb]));
-        pkB[rb][t] = pack2<BF16>(e0, e1);
-        if constexpr (BF16) {
-          tl[rb] += e0 + e1;
-        } else {
-          tl[rb] = add_pair_f16(pkB[rb][t], tl[rb]);
-        }
+    const float m_neg = -m_sub;
+    float t_acc = 0.0f;
+    auto exp_pair = [&](int t) __attribute__((always_inline)) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[2 * t], c_log2, m_neg));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[2 * t + 1], c_log2, m_neg));
+      pkB[t] = pack2<BF16>(e0, e1);
+      if constexpr (BF16) {
+        t_acc += e0 + e1;
+      } else {
+        t_acc = add_pair_f16(pkB[t], t_acc);
       }
     };
     u32x4 bo[2][2];
     p_operands(pkA, bo);
-    u32x4 va[3];
-    va[0] = vread(0);
-    va[1] = vread(1);
-    int pr = 0;
+    constexpr int VP = 2;                         // V^T steps read ahead
+    u32x4 va[VP + 1];
+#pragma unroll
+    for (int st = 0; st < VP; ++st) va[st] = vread(st);
+    int pair = 0;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      if (st + 2 < NSTEP) va[(st + 2) % 3] = vread(st + 2);
+      if (st + VP < NSTEP) va[(st + VP) % (VP + 1)] = vread(st + VP);
       const int e = st / DB, d = st % DB;
-      const u32x4 b0 = bo[e][0], b1 = bo[e][1];
-      __builtin_amdgcn_sched_barrier(0);
-#if SDPA_W64_ASM
-      mfma32_acc<BF16>(acc[0][d], va[st % 3], b0);
-#else
-      acc[0][d] = mfma32<BF16>(va[st % 3], b0, acc[0][d]);
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-      exp_pairs(pr);
-      pr += PAIRS_PER_MFMA;
-      __builtin_amdgcn_sched_barrier(0);
-#if SDPA_W64_ASM
-      mfma32_acc<BF16>(acc[1][d], va[st % 3], b1);
-#else
-      acc[1][d] = mfma32<BF16>(va[st % 3], b1, acc[1][d]);
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-      exp_pairs(pr);
-      pr += PAIRS_PER_MFMA;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int m = 2 * st + rb;
+        __builtin_amdgcn_sched_barrier(0);
+        mfma32_acc<BF16>(acc[rb][d], va[st % (VP + 1)], bo[e][rb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (; pair < 8 && pair * NM < (m + 1) * 8; ++pair) exp_pair(pair);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
+    tl = t_acc;
   };
 
-  // One body for masked and unmasked tiles (the masks are small conditional
-  // regions): two specialised copies of the tile would meet at a join where
-  // the allocator moves the accumulators between registers.
-  auto compute_tile = [&](int j, const uint8_t* ks, bool need_mask) __attribute__((always_inline)) {
+  // ---- main loop: a three-stage LDS ring and a software pipeline over the
+  // 32-key blocks ("units") of the tiles. Tile j's body runs, for this wave:
+  //   g1: S of unit (j,1)                      | exponentials of unit (j,0), row block 1
+  //       settle unit (j,0)
+  //   g2: P V of unit (j,0)                    | exponentials of unit (j,1), row block 0
+  //       barrier (tile j+1 resident); loads of tile j+2 into the stage of tile j-1
+  //   g3: S of unit (j+1,0)                    | exponentials of unit (j,1), row block 1
+  //       settle unit (j,1)
+  //   g4: P V of unit (j,1)                    | exponentials of unit (j+1,0), row block 0
+  // so every group of matrix operations has softmax work beside it. One barrier
+  // per tile; each stage is its own array and the loop is unrolled by three, so
+  // the compiler can tell LDS reads from the in-flight direct loads apart.
+  // Tiles past this wave's causal range are skipped (the wave still joins the
+  // barriers and issues its share of the loads); on a wave's last tile, g3/g4
+  // work on stale LDS and their results are never used.
+  f32x16 s_c[2];                 // scores of unit (j, 0)
+  uint32_t pk_c[2][8];
+  float tl_c[2];
+  const int nw = CAUSAL ? min(n_kv, (wq0 + 63) / BN + 1) : n_kv;   // tiles this wave computes
+  auto need_mask = [&](int jj) __attribute__((always_inline)) {
+    return (jj * BN + BN > L) || (CAUSAL && jj * BN + BN - 1 > wq0);
+  };
+  auto stage = [&](int st) __attribute__((always_inline)) -> uint8_t* {
+    return st == 0 ? smem0 : (st == 1 ? smem1 : smem2);
+  };
+  auto body = [&](int jj, auto st_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_tag)::value;
+    const uint8_t* ks = stage(ST);
     const uint8_t* vs = ks + TILEB;
-    const int key0 = j * BN;
-    f32x16 s0[2], s1[2];
-    uint32_t pk0[2][8], pk1[2][8];
-    float tl0[2], tl1[2];
-    qk_block(ks, 0, s0);
-    if (need_mask) mask_block(key0, 0, s0);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) tl0[rb] = exps(s0[rb], pk0[rb], m_run[rb]);
-    qk_block(ks, 1, s1);
-    if (need_mask) mask_block(key0, 1, s1);
-    settle(s0, pk0, tl0);
-#if SDPA_W64_OVERLAP
-    pv0_with_exps1(vs, pk0, s1, pk1, tl1);
-#else
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) tl1[rb] = exps(s1[rb], pk1[rb], m_run[rb]);
-    pv_block(vs, 0, pk0);
-#endif
-    settle(s1, pk1, tl1);
-    pv_block(vs, 1, pk1);
-  };
-  auto tile = [&](int j, const uint8_t* ks) __attribute__((always_inline)) {
-    const int key0 = j * BN;
-    if (CAUSAL && key0 > wq0 + 63) return;      // no row of this wave sees the tile
-    compute_tile(j, ks, (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0));
+    const uint8_t* ks_next = stage((ST + 1) % 3);
+    const bool act = jj < nw;
+    const int key0 = jj * BN;
+    f32x16 s_n[2];
+    uint32_t pk_n[2][8];
+    float tl_n[2];
+    if (act) {
+      qk_block(ks, 1, s_n);
+      tl_c[1] = exps(s_c[1], pk_c[1], m_run[1]);
+      settle(s_c, pk_c, tl_c);
+      if (need_mask(jj)) mask_block(key0, 1, s_n);
+      pv_with_exps(vs, 0, pk_c, s_n[0], pk_n[0], tl_n[0], m_run[0]);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    if (jj + 2 < n_kv) issue_tile(jj + 2, (ST + 2) % 3);
+    if (act) {
+      qk_block(ks_next, 0, s_c);
+      tl_n[1] = exps(s_n[1], pk_n[1], m_run[1]);
+      settle(s_n, pk_n, tl_n);
+      if (need_mask(jj + 1)) mask_block(key0 + BN, 0, s_c);
+      pv_with_exps(vs, 1, pk_n, s_c[0], pk_c[0], tl_c[0], m_run[0]);
+    }
   };
 
-  // Pairs of tiles, then an odd last tile after the loop: no exit in the
-  // middle of the loop body, so the accumulators keep one register assignment
-  // through both halves (a mid-body exit made the allocator copy them at the
-  // join, which would read assembly-MFMA results without wait states).
   issue_tile(0, 0);
+  if (n_kv > 1) issue_tile(1, 1);
   wait_vmem_all();
   __syncthreads();
-  int j = 0;
-#pragma unroll 1
-  for (; j + 1 < n_kv; j += 2) {
-    issue_tile(j + 1, 1);
-    tile(j, smem0);
-    wait_vmem_all();
-    __syncthreads();
-    if (j + 2 < n_kv) issue_tile(j + 2, 0);
-    tile(j + 1, smem1);
-    wait_vmem_all();
-    __syncthreads();
+  if (0 < nw) {
+    qk_block(smem0, 0, s_c);
+    if (need_mask(0)) mask_block(0, 0, s_c);
+    tl_c[0] = exps(s_c[0], pk_c[0], m_run[0]);
   }
-  if (j < n_kv) tile(j, smem0);
+#pragma unroll 1
+  for (int j = 0; j < n_kv; j += 3) {
+    body(j, std::integral_constant<int, 0>{});
+    if (j + 1 < n_kv) body(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < n_kv) body(j + 2, std::integral_constant<int, 2>{});
+  }
 
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(og, q_rows * tok_bytes);
 #pragma unroll
@@ -1023,13 +1008,18 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
 // better. Both share every per-row arithmetic step, so results are identical.
 constexpr long long kBigProblemTiles = 2048;
 
-static int choose_waves(const FwdParams& p, bool varlen) {
-  // ATTN_WAVES=4 or 8 overrides the choice (used by tests to cover both).
+// Returns 4 or 8 (32-row waves) or 64 (the 64-row-wave kernel). The 64-row
+// waves are used for D = 64 without causality, the one case where they
+// measured faster (B4 H12 S2048 D64 fp16: +5 to +10 %); with causality, and at
+// D = 128 (LLaMA-shaped layer: about -9 %), the 32-row waves win.
+static int choose_waves(const FwdParams& p, int D, bool causal, bool varlen) {
+  // ATTN_WAVES=4, 8 or w64 overrides the choice (used by tests to cover all three).
   if (const char* e = std::getenv("ATTN_WAVES")) {
     if (e[0] == '4' && e[1] == '\0') return 4;
     if (e[0] == '8' && e[1] == '\0') return 8;
     if (e[0] == 'w' && e[1] == '6' && e[2] == '4' && e[3] == '\0') return 64;
   }
+  if (D == 64 && !causal) return 64;
   const long long bh = varlen ? p.H : (long long)p.B * p.H;
   const long long tiles256 = varlen ? (long long)p.S / 256 + p.B : ((long long)p.S + 255) / 256;
   return tiles256 * bh >= kBigProblemTiles ? 8 : 4;
@@ -1066,7 +1056,7 @@ static hipError_t launch_nw(const FwdParams& p, hipStream_t stream) {
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
     return launch_one<D, BF16, CAUSAL, VARLEN, 4, true>(p, stream);
   }
-  const int w = choose_waves(p, VARLEN);
+  const int w = choose_waves(p, D, CAUSAL, VARLEN);
   if (w == 64) return launch_w64<D, BF16, CAUSAL, VARLEN>(p, stream);
   return w == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, stream)
                 : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, stream);
