@@ -41,8 +41,10 @@
 // per SIMD with the output accumulators in AGPRs (their MFMAs are inline
 // assembly, guarded by explicit wait states that the build verifies on the
 // emitted code), and software-pipelines the 32-key blocks of a three-stage LDS
-// ring so that every group of MFMAs has softmax work beside it. It is the
-// default for D = 64 without causality.
+// ring so that every group of MFMAs has softmax work beside it. It halves the
+// LDS reads but, with a single wave per SIMD, exposes every latency the second
+// wave used to hide; under sustained load it is slower than the 32-row kernel
+// on every benchmark workload and runs only when ATTN_WAVES=w64 asks for it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1009,17 +1011,17 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
 constexpr long long kBigProblemTiles = 2048;
 
 // Returns 4 or 8 (32-row waves) or 64 (the 64-row-wave kernel). The 64-row
-// waves are used for D = 64 without causality, the one case where they
-// measured faster (B4 H12 S2048 D64 fp16: +5 to +10 %); with causality, and at
-// D = 128 (LLaMA-shaped layer: about -9 %), the 32-row waves win.
-static int choose_waves(const FwdParams& p, int D, bool causal, bool varlen) {
+// waves are never chosen by default: under sustained load they measured
+// slower on every benchmark workload (LLaMA-shaped layer about -9 %,
+// B4 H12 S2048 D64 -4 % without and -27 % with causality), so they are only
+// reachable through ATTN_WAVES=w64.
+static int choose_waves(const FwdParams& p, bool varlen) {
   // ATTN_WAVES=4, 8 or w64 overrides the choice (used by tests to cover all three).
   if (const char* e = std::getenv("ATTN_WAVES")) {
     if (e[0] == '4' && e[1] == '\0') return 4;
     if (e[0] == '8' && e[1] == '\0') return 8;
     if (e[0] == 'w' && e[1] == '6' && e[2] == '4' && e[3] == '\0') return 64;
   }
-  if (D == 64 && !causal) return 64;
   const long long bh = varlen ? p.H : (long long)p.B * p.H;
   const long long tiles256 = varlen ? (long long)p.S / 256 + p.B : ((long long)p.S + 255) / 256;
   return tiles256 * bh >= kBigProblemTiles ? 8 : 4;
@@ -1056,7 +1058,7 @@ static hipError_t launch_nw(const FwdParams& p, hipStream_t stream) {
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
     return launch_one<D, BF16, CAUSAL, VARLEN, 4, true>(p, stream);
   }
-  const int w = choose_waves(p, D, CAUSAL, VARLEN);
+  const int w = choose_waves(p, VARLEN);
   if (w == 64) return launch_w64<D, BF16, CAUSAL, VARLEN>(p, stream);
   return w == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, stream)
                 : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, stream);
