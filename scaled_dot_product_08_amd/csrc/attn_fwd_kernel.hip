@@ -612,12 +612,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 // read 256 KB of K and V per 64-key tile, about what LDS delivers in the time
 // the matrix cores take for the tile). With 512 registers per lane available
 // at one wave per SIMD, the 2*D/32 output accumulators sit in the
-// accumulation registers. Inside a tile the two 32-key blocks form a short
-// software pipeline that a single wave can overlap on its own: the
-// exponentials of key block 0 are independent of the scores of block 1, and
-// those of block 1 of P V over block 0. The per-row arithmetic (optimistic
-// exponentials, lazy maximum, row sums) is that of the 32-row kernel, applied
-// per 32-key block instead of per 64-key tile.
+// accumulation registers. The 32-key blocks of consecutive tiles form a
+// software pipeline over a three-stage LDS ring (see the main loop) so that a
+// single wave has softmax work beside every group of matrix operations. The
+// per-row arithmetic (optimistic exponentials, lazy maximum, row sums) is that
+// of the 32-row kernel, applied per 32-key block instead of per 64-key tile.
+// Slower than the 32-row kernel under sustained load (one wave per SIMD
+// exposes the latencies a second wave hides); reachable with ATTN_WAVES=w64.
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256, 1) void attn_fwd_w64_kernel(FwdParams p) {
   constexpr int NWAVES = 4;
