@@ -120,6 +120,20 @@ def test_config_varlen_sampled():
     assert torch.isfinite(o.float()).all()
 
 
+@pytest.mark.parametrize("name", ["mha", "mha_causal", "llama", "long"])
+def test_config_64_row_waves(name, monkeypatch):
+    """The opt-in 64-row-wave kernel at the benchmark sizes: whole outputs for B4 H12 S2048 D64,
+    sampled rows of the LLaMA-shaped layer and of the 64K-token sequence."""
+    monkeypatch.setenv("ATTN_WAVES", "w64")
+    cfg = synth.CONFIGS[name]
+    say(name, "64-row waves", cfg.describe())
+    if name.startswith("mha"):
+        inp = synth.make_inputs(cfg)
+        check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
+    else:
+        _sampled_padded(cfg, rows_per_head=32 if name == "llama" else 48)
+
+
 # ---- reduced shapes: every tile boundary, ragged tails, both dtypes / D ----------
 
 SHAPES = [
