@@ -231,11 +231,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   const int logical = (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
   const int nbh = VARLEN ? p.H : p.B * p.H;
   const int nt = p.n_qtiles;
-  const int grp = logical / (HEAD_GROUP * nt);
-  const int in_grp = min(HEAD_GROUP, nbh - grp * HEAD_GROUP);
-  const int rem = logical - grp * (HEAD_GROUP * nt);
+  // Heads per group: 2 for the plain 128-row tiles (B4 H12 S2048 D64 causal
+  // measured 6-7 % faster than with 4, non-causal within 1 %), 4 otherwise.
+  constexpr int HGRP = (NW == 4 && !EXT) ? 2 : HEAD_GROUP;
+  const int grp = logical / (HGRP * nt);
+  const int in_grp = min(HGRP, nbh - grp * HGRP);
+  const int rem = logical - grp * (HGRP * nt);
   const int rank = rem / in_grp;
-  const int bh = grp * HEAD_GROUP + (rem - rank * in_grp);
+  const int bh = grp * HGRP + (rem - rank * in_grp);
   const int h = bh % p.H;
   const int b = VARLEN ? 0 : bh / p.H;
   int vt = nt - 1 - rank;
