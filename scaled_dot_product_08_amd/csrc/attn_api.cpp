@@ -148,6 +148,7 @@ static int fwd_common(const void* q, const void* k, const void* v, void* out, fl
   p.H = H;
   p.S = S;
   p.n_qtiles = 0;   // set by the launcher for the workgroup size it picks
+  p.head_group = 0;  // set by the launcher
   const float log2e = 1.4426950408889634f;
   if (scale > 0.0f) {
     p.c_log2 = scale * log2e;

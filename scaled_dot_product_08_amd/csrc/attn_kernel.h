@@ -16,6 +16,7 @@ struct FwdParams {
   int H;
   int S;                    // sequence length (padded) or total tokens T (packed)
   int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed); set at launch
+  int head_group;           // heads whose query tiles one XCD interleaves (128-row tiles); set at launch
   float c_log2;             // |scale| * log2(e), or log2(e) when scale == 0
   int q_mode;               // 0: scale > 0, 1: scale < 0 (use -Q), 2: scale == 0 (Q := 0)
   int window;               // sliding-window width in keys (0: none)
