@@ -59,9 +59,10 @@ enum {
  *   q, k, v, out : contiguous (T, H, D) arrays of `dtype`.
  *   cu_seqlens   : int32 DEVICE array of B+1 prefix offsets, cu_seqlens[0]=0,
  *                  non-decreasing, cu_seqlens[B]=T (zero-length sequences
- *                  allowed). Its contents are a precondition; set the
- *                  environment variable ATTN_DEBUG=1 to validate them (this
- *                  synchronizes the stream) before the launch.
+ *                  allowed). Its contents are a precondition; with the
+ *                  environment variable ATTN_DEBUG=1 set when the library
+ *                  first checks it, every packed call validates them first
+ *                  (this synchronizes the stream).
  *   lse          : contiguous (H, T) float32, or NULL.
  *
  * Semantics: self-attention (query and key lengths equal, same head count
@@ -82,15 +83,30 @@ enum {
  * Errors: ATTN_ERR_* argument codes are returned synchronously with nothing
  * enqueued; ATTN_ERR_LAUNCH if the launch fails (hipGetLastError).
  *
- * Tuning: the library picks 128- or 256-row query tiles per workgroup from
- * the problem size; ATTN_WAVES=4 / ATTN_WAVES=8 forces 128 / 256 (for D = 128
- * the results are bitwise identical either way; for D = 64 the 128-row
- * kernel walks 128-key tiles instead of 64 and the results differ by
- * rounding only).
+ * The library picks 128- or 256-row query tiles per workgroup from the
+ * problem size (attn_fwd_tuned fixes the choice).
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int S, int D, int causal, float scale, int dtype,
              const int32_t* cu_seqlens, void* stream);
+
+/*
+ * attn_fwd_tuned -- attn_fwd with its launch shape fixed by the caller (for
+ * tuning sweeps and for tests that must reach every kernel instance).
+ *
+ * Same arguments, layouts, semantics and errors as attn_fwd, plus:
+ *   tile_rows  : query rows per workgroup, 128 or 256; 0 lets the library
+ *                choose as attn_fwd does. Anything else: ATTN_ERR_UNSUPPORTED.
+ *   head_group : how many (batch, head) pairs one XCD interleaves the query
+ *                tiles of (clamped to B*H, or H when packed); 0 lets the
+ *                library choose. Negative: ATTN_ERR_SHAPE.
+ * Results do not depend on head_group. They do not depend on tile_rows for
+ * D = 128; for D = 64 the 128-row tiles walk 128 keys per step instead of
+ * 64, so the sums are grouped differently and results differ by rounding.
+ */
+int attn_fwd_tuned(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int H, int S, int D, int causal, float scale, int dtype,
+                   const int32_t* cu_seqlens, int tile_rows, int head_group, void* stream);
 
 /*
  * attn_fwd_ext -- attn_fwd with the mask and bias variants.

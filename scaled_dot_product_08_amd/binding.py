@@ -18,7 +18,7 @@ STATUS = {
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
@@ -44,6 +44,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_tuned.restype = ctypes.c_int
+    lib.attn_fwd_tuned.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_ext.restype = ctypes.c_int
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -87,6 +90,14 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scal
     """Direct call with integer pointers; returns the status code."""
     return load_library().attn_fwd(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
                                    int(D), int(causal), float(scale), int(dtype), cu_ptr, stream_ptr)
+
+
+def attn_fwd_tuned_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
+                       cu_ptr, tile_rows, head_group, stream_ptr) -> int:
+    """Direct call of attn_fwd_tuned with integer pointers; returns the status code."""
+    return load_library().attn_fwd_tuned(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H),
+                                         int(S), int(D), int(causal), float(scale), int(dtype),
+                                         cu_ptr, int(tile_rows), int(head_group), stream_ptr)
 
 
 def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
@@ -185,13 +196,14 @@ def _stream_ptr(stream):
 
 def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None,
              cu_seqlens=None, stream=None, window: int = 0, n_global: int = 0,
-             alibi_slopes=None) -> None:
+             alibi_slopes=None, tile_rows: int = 0, head_group: int = 0) -> None:
     """Call attn_fwd on torch device tensors.
 
     Padded: q,k,v,out (B,S,H,D), lse (B,H,S) fp32 or None.
     Packed: q,k,v,out (T,H,D), cu_seqlens int32 (nseq+1,), lse (H,T) or None.
     ``scale=None`` means 1/sqrt(D) rounded to float32. ``window``, ``n_global`` and
-    ``alibi_slopes`` (float32 device tensor of H slopes) call attn_fwd_ext.
+    ``alibi_slopes`` (float32 device tensor of H slopes) call attn_fwd_ext;
+    ``tile_rows`` / ``head_group`` (launch shape, 0 = automatic) call attn_fwd_tuned.
     """
     _check_tensors(("q", "k", "v", "out"), (q, k, v, out))
     if cu_seqlens is None:
@@ -210,7 +222,14 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     lse_ptr = None if lse is None else lse.data_ptr()
-    if window or n_global or alibi_slopes is not None:
+    masks = bool(window or n_global or alibi_slopes is not None)
+    if masks and (tile_rows or head_group):
+        raise ValueError("the mask/bias variants take no launch-shape arguments")
+    if tile_rows or head_group:
+        st = attn_fwd_tuned_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
+                                tile_rows, head_group, _stream_ptr(stream))
+    elif masks:
         al = None
         if alibi_slopes is not None:
             if (alibi_slopes.dtype != torch_float32() or alibi_slopes.numel() != H
@@ -231,7 +250,7 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
 
 def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
         with_lse: bool = True, stream=None, window: int = 0, n_global: int = 0,
-        alibi_slopes=None):
+        alibi_slopes=None, tile_rows: int = 0, head_group: int = 0):
     """Allocate O (and LSE) with torch and run attn_fwd. Returns (O, LSE or None)."""
     import torch
     out = torch.empty_like(q)
@@ -244,7 +263,8 @@ def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
             T, H, _ = q.shape
             lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, out, lse, causal=causal, scale=scale, cu_seqlens=cu_seqlens, stream=stream,
-             window=window, n_global=n_global, alibi_slopes=alibi_slopes)
+             window=window, n_global=n_global, alibi_slopes=alibi_slopes, tile_rows=tile_rows,
+             head_group=head_group)
     return out, lse
 
 

@@ -22,9 +22,14 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// ATTN_DEBUG=1 (read once, at the first call that could use it) makes the
+// packed-mode entry points validate cu_seqlens first, synchronizing.
 bool debug_enabled() {
-  const char* e = std::getenv("ATTN_DEBUG");
-  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  static const bool on = [] {
+    const char* e = std::getenv("ATTN_DEBUG");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
 }
 
 // Validation shared by attn_fwd; no HIP call. Fills the grid size on success.
@@ -126,7 +131,7 @@ int attn_check_cu_seqlens(const int32_t* cu_seqlens, int B, int T, void* stream)
 static int fwd_common(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                       int H, int S, int D, int causal, float scale, int dtype,
                       const int32_t* cu_seqlens, int window, int n_global, const float* alibi,
-                      void* stream) {
+                      const sdpa08::FwdTuning& tuning, void* stream) {
   long long grid = 0;
   const int st = validate(q, k, v, out, lse, B, H, S, D, scale, dtype, cu_seqlens, &grid);
   if (st != ATTN_OK) return st;
@@ -164,7 +169,7 @@ static int fwd_common(const void* q, const void* k, const void* v, void* out, fl
   p.n_global = n_global;
   p.alibi = alibi;
   const hipError_t e = sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
-                                          reinterpret_cast<hipStream_t>(stream));
+                                          tuning, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -172,7 +177,19 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int S, int D, int causal, float scale, int dtype, const int32_t* cu_seqlens,
              void* stream) {
   return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, 0, 0,
-                    nullptr, stream);
+                    nullptr, sdpa08::FwdTuning{}, stream);
+}
+
+int attn_fwd_tuned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int H, int S, int D, int causal, float scale, int dtype,
+                   const int32_t* cu_seqlens, int tile_rows, int head_group, void* stream) {
+  if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256) return ATTN_ERR_UNSUPPORTED;
+  if (head_group < 0) return ATTN_ERR_SHAPE;
+  sdpa08::FwdTuning t;
+  t.tile_rows = tile_rows;
+  t.head_group = head_group;
+  return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, 0, 0,
+                    nullptr, t, stream);
 }
 
 int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -181,7 +198,7 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                  const float* alibi_slopes, void* stream) {
   if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) return ATTN_ERR_ALIGN;
   return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, window,
-                    n_global, alibi_slopes, stream);
+                    n_global, alibi_slopes, sdpa08::FwdTuning{}, stream);
 }
 
 size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int num_splits) {

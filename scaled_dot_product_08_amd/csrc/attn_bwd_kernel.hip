@@ -28,106 +28,16 @@
 #include <stdint.h>
 
 #include "attn_bwd.h"
+#include "gfx950_util.h"
 
 namespace sdpa08 {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int NW = 4;           // waves per workgroup
 constexpr int BM = kBwdTileRows; // rows owned by a workgroup (32 per wave)
 constexpr int BN = 64;          // rows per streamed LDS tile
 constexpr int HEAD_GROUP = 4;   // heads whose tiles are interleaved on one XCD
-constexpr int NXCD = 8;
-constexpr int BUF_FLAGS = 0x00020000;
 constexpr float LOG2E = 1.4426950408889634f;
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  f32x2 v = {x, y};
-  if constexpr (BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
-}
-
-// The two 16-bit values of a packed pair, widened to fp32 exactly.
-template <bool BF16>
-__device__ __forceinline__ f32x2 unpack2(uint32_t w) {
-  if constexpr (BF16) {
-    return f32x2{__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u)};
-  } else {
-    return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
-  }
-}
-
-__device__ __forceinline__ int swap23(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
-// 16-byte chunk swizzle of an LDS tile row (conflict-free for the operand
-// reads, the transposing reads and the direct loads; see the forward).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {
-    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-}
-
-// Combine the two halves of a wave: lane i gets op(x[i % 32], x[i % 32 + 32]).
-// v_permlane32_swap_b32 a, b exchanges the upper half of a with the lower
-// half of b; with a = b = x, afterwards {a, b} = {x[i % 32], x[i % 32 + 32]}
-// at every lane (measured), in some order, and max and + are symmetric. It is
-// written in assembly because the compiler's model of the builtin's second
-// result folds it into the first; the s_nops on either side cover the
-// VALU-to-permlane and permlane-to-VALU hazards.
-__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
-  a = x;
-  b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float half_max(float x) {
-  float a, b;
-  swap_halves(x, a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float half_sum(float x) {
-  float a, b;
-  swap_halves(x, a, b);
-  return a + b;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
-}
-
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // Which (sequence, head, 128-row tile) a workgroup owns. Workgroup i runs on
 // XCD i % 8; each XCD gets a contiguous run of the logical order, which walks
@@ -139,11 +49,7 @@ struct Item {
 
 template <bool VARLEN>
 __device__ __forceinline__ bool map_item(const BwdParams& p, bool ascending, Item& it) {
-  const int G = gridDim.x;
-  const int xcd = blockIdx.x % NXCD;
-  const int local = blockIdx.x / NXCD;
-  const int gq = G / NXCD, gr = G % NXCD;
-  const int logical = (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int nbh = VARLEN ? p.H : p.B * p.H;
   const int nt = p.n_tiles;
   const int grp = logical / (HEAD_GROUP * nt);

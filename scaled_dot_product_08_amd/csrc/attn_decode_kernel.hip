@@ -35,27 +35,15 @@
 #include <stdint.h>
 
 #include "attn_decode.h"
+#include "gfx950_util.h"
 
 namespace sdpa08 {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-#ifndef SDPA_DEC_UNROLL
-#define SDPA_DEC_UNROLL 16
-#endif
-#ifndef SDPA_DEC_AUX
-#define SDPA_DEC_AUX 2      // non-temporal: the cache is streamed once
-#endif
-
 constexpr int NWAVE = 4;          // waves per workgroup
-constexpr int UNROLL = SDPA_DEC_UNROLL;   // cache-row steps per wave per iteration (loads in flight)
-constexpr int LOAD_AUX = SDPA_DEC_AUX;    // cache policy bits of the cache loads
-constexpr int NXCD = 8;           // workgroups go round-robin over the 8 XCDs
+constexpr int UNROLL = 16;        // cache-row steps per wave per iteration (loads in flight)
+constexpr int LOAD_AUX = 2;       // cache policy bits of the cache loads: non-temporal, streamed once
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
-constexpr int BUF_FLAGS = 0x00020000;   // raw buffer descriptor word 3 (32-bit dwords)
 constexpr int MAX_SPLITS = 256;
 
 template <int D>
@@ -67,10 +55,6 @@ struct Geo {
   static constexpr int KEYS_WG = KEYS_WAVE * NWAVE;
   static constexpr int NPART = NWAVE * KPW;        // partial results per workgroup
 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
-}
 
 // x + (x from the lane given by a DPP pattern), within rows of 16 lanes.
 template <int CTRL>
@@ -138,12 +122,7 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_decode_split_kernel(DecodePar
   // Workgroup i runs on XCD i % 8; renumber so that each XCD owns a
   // contiguous run of (row, split) items (the Sq query rows that share a
   // split are neighbours, so their repeated cache reads meet in one L2).
-  const int Gn = gridDim.x;
-  const int xcd = blockIdx.x % NXCD;
-  const int local = blockIdx.x / NXCD;
-  const int gq = Gn / NXCD, gr = Gn % NXCD;
-  const int logical =
-      (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int qi = logical % p.Sq;
   const int rest = logical / p.Sq;
   const int split = rest % p.n_splits;

@@ -35,21 +35,10 @@
 #include <stdint.h>
 
 #include "attn_fp8.h"
+#include "gfx950_util.h"
 
 namespace sdpa08 {
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int D = 128;
 constexpr int NW = 4;             // waves per workgroup
@@ -61,25 +50,13 @@ constexpr int STAGEB = 2 * TILEB; // K tile + V tile
 constexpr int LDW = TILEB / 1024 / NW;
 constexpr int DB = D / 32;        // 32-column blocks of O^T
 constexpr int HEAD_GROUP = 4;
-constexpr int NXCD = 8;
 constexpr float LAZY_RESCALE_LOG2 = 4.0f;
 constexpr float E4M3_MAX = 448.0f;       // largest finite E4M3 value
 constexpr float P_SHIFT_LOG2 = 4.0f;   // P is quantised as P * 2^4
-constexpr int BUF_FLAGS = 0x00020000;
 constexpr int E8M0_ONE = 127;          // block scale 2^0
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, E8M0_ONE, 0, E8M0_ONE);
-}
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  f32x2 v = {x, y};
-  if constexpr (BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-  }
 }
 
 // 16-byte chunk permutation of a 128-byte LDS row (see the header comment).
@@ -87,34 +64,6 @@ __device__ __forceinline__ int swz8(int r) {
   return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1);
 }
 
-// Combine the two halves of a wave: lane i gets op(x[i % 32], x[i % 32 + 32]).
-// v_permlane32_swap_b32 a, b exchanges the upper half of a with the lower
-// half of b; with a = b = x, afterwards {a, b} = {x[i % 32], x[i % 32 + 32]}
-// at every lane (measured), in some order, and max and + are symmetric. It is
-// written in assembly because the compiler's model of the builtin's second
-// result folds it into the first; the s_nops on either side cover the
-// VALU-to-permlane and permlane-to-VALU hazards.
-__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
-  a = x;
-  b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ float half_max(float x) {
-  float a, b;
-  swap_halves(x, a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float half_sum(float x) {
-  float a, b;
-  swap_halves(x, a, b);
-  return a + b;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, BUF_FLAGS);
-}
-
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 template <bool OUT_BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
@@ -127,11 +76,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   const int hh = lane >> 5;
 
   // ---- (sequence, head, query tile) of this workgroup, as the 16-bit kernel
-  const int G = gridDim.x;
-  const int xcd = blockIdx.x % NXCD;
-  const int local = blockIdx.x / NXCD;
-  const int gq = G / NXCD, gr = G % NXCD;
-  const int logical = (xcd < gr) ? xcd * (gq + 1) + local : gr * (gq + 1) + (xcd - gr) * gq + local;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int nbh = VARLEN ? p.H : p.B * p.H;
   const int nt = p.n_qtiles;
   const int grp = logical / (HEAD_GROUP * nt);

@@ -16,7 +16,7 @@ struct FwdParams {
   int H;
   int S;                    // sequence length (padded) or total tokens T (packed)
   int n_qtiles;             // query tiles per (batch, head), or virtual tiles (packed); set at launch
-  int head_group;           // heads whose query tiles one XCD interleaves (128-row tiles); set at launch
+  int head_group;           // heads whose query tiles one XCD interleaves; set at launch
   float c_log2;             // |scale| * log2(e), or log2(e) when scale == 0
   int q_mode;               // 0: scale > 0, 1: scale < 0 (use -Q), 2: scale == 0 (Q := 0)
   int window;               // sliding-window width in keys (0: none)
@@ -28,9 +28,15 @@ struct FwdParams {
 int max_query_tile_rows();
 int min_query_tile_rows();
 
+// Launch shape chosen by the caller instead of by problem size (0 = automatic).
+struct FwdTuning {
+  int tile_rows = 0;        // query rows per workgroup: 128 or 256
+  int head_group = 0;       // heads whose query tiles one XCD interleaves
+};
+
 // Launch the kernel instance for (D, dtype, causal, packed) on `stream`; picks
-// the workgroup size, fills n_qtiles and sizes the grid.
+// the workgroup size, fills n_qtiles and head_group and sizes the grid.
 hipError_t launch_fwd(const FwdParams& p, int D, bool bf16, bool causal, bool varlen,
-                      hipStream_t stream);
+                      const FwdTuning& tuning, hipStream_t stream);
 
 }  // namespace sdpa08

@@ -28,3 +28,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With ATTN_PARITY_REPORT=<path>, write the parity margins the GPU tests recorded."""
+    path = os.environ.get("ATTN_PARITY_REPORT")
+    if not path:
+        return
+    try:
+        import gpu_util
+    except Exception:
+        return
+    if not gpu_util.MARGINS:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"exitstatus": int(exitstatus), "cases": gpu_util.MARGINS}, f, indent=1)

@@ -34,3 +34,38 @@ def max_abs(a, b) -> float:
     if np.isnan(d).any():
         return float("inf")
     return float(d.max()) if d.size else 0.0
+
+
+# ---- parity margins ------------------------------------------------------------
+# Tests that compare a workload with the oracle record their largest errors here;
+# conftest.py writes them out at the end of the session when ATTN_PARITY_REPORT
+# names a file.
+MARGINS: list = []
+
+
+def rne_floor(oref: np.ndarray, dtype: str) -> float:
+    """max |RNE(oref) - oref|: the error that rounding the exact output to the storage
+    type alone already makes (round to nearest even, computed from float64)."""
+    x = np.asarray(oref, np.float64)
+    if x.size == 0:
+        return 0.0
+    if dtype == "fp16":
+        r = x.astype(np.float16).astype(np.float64)
+    else:
+        # bf16 keeps 8 significant bits: round to a multiple of 2^(e-7), ties to even
+        # (numpy's round is half-to-even); zeros and subnormal-range values stay as is.
+        ax = np.abs(x)
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+        ulp = np.exp2(e - 7)
+        r = np.where(ax > 0, np.round(x / ulp) * ulp, x)
+    return float(np.abs(r - x).max())
+
+
+def record(case: str, dtype: str, eo: float, el: float, oref=None, n_rows: int | None = None,
+           floor: float | None = None, tol_o: float | None = None):
+    """Remember one case's largest errors (and the rounding floor of its exact output)."""
+    if floor is None and oref is not None:
+        floor = rne_floor(oref, dtype)
+    MARGINS.append({"case": case, "dtype": dtype, "max_abs_dO": eo, "max_abs_dLSE": el,
+                    "tol_O": TOL_O[dtype] if tol_o is None else tol_o, "tol_LSE": TOL_LSE,
+                    "rne_floor_O": floor, "rows_checked": n_rows})

@@ -29,6 +29,40 @@ def test_max_heads():
     assert eo <= TOL_O["fp16"] and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("tile_rows", [128, 256])
+def test_max_heads_d128_full_tiles(tile_rows):
+    """H = 65535 at D = 128 with whole 128/256-row query tiles: a tile spans up to
+    256 * 65535 * 256 bytes, 64 KB under 2^32, the largest byte range a buffer descriptor of
+    the kernel covers. Four heads carry seeded inputs and are checked against the oracle; every
+    other head has Q = K = V = 0, so its output must be exactly 0 and exp(LSE) the count of
+    visible keys (i + 1 under causality), which checks every head's tile mapping and offsets."""
+    B, S, H, D = 1, 256, 65535, 128
+    say(f"max heads D=128 B={B} S={S} H={H} tile_rows={tile_rows}")
+    q = torch.zeros((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    v = torch.zeros_like(q)
+    heads = [0, 1, 32768, 65534]
+    qb, kb, vb = synth.normal_qkv((B, S, len(heads), D), "bf16", 8050)
+    for i, h in enumerate(heads):
+        q[:, :, h] = to_dev(np.ascontiguousarray(qb[:, :, i]), "bf16")
+        k[:, :, h] = to_dev(np.ascontiguousarray(kb[:, :, i]), "bf16")
+        v[:, :, h] = to_dev(np.ascontiguousarray(vb[:, :, i]), "bf16")
+    o, lse = binding.fwd(q, k, v, causal=True, scale=scale_of(D), tile_rows=tile_rows)
+    torch.cuda.synchronize()
+    f = [synth.bits_to_f64(x, "bf16") for x in (qb, kb, vb)]
+    oref, lref = attention(*f, causal=True, scale=scale_of(D))
+    eo = max_abs(to_f64(o[:, :, heads]), oref)
+    el = max_abs(lse[:, heads].cpu().numpy(), lref)
+    say(f"    seeded heads max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+    zero = torch.ones(H, dtype=torch.bool, device="cuda")
+    zero[heads] = False
+    assert (o[:, :, zero] == 0).all().item()
+    counts = torch.exp(lse[:, zero].double()).round()
+    expect = torch.arange(1, S + 1, dtype=torch.float64, device="cuda")
+    assert (counts == expect).all().item()
+
+
 def test_long_single_sequence():
     """One 262144-token sequence, one head, causal: 2048 query tiles of one (b, h)."""
     B, S, H, D = 1, 262144, 1, 64

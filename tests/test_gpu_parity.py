@@ -8,34 +8,38 @@ import pytest
 import torch
 
 import synth
-from gpu_util import TOL_LSE, TOL_O, max_abs, say, scale_of, to_dev, to_f64
+from gpu_util import TOL_LSE, TOL_O, max_abs, record, rne_floor, say, scale_of, to_dev, to_f64
 from oracle import attention, attention_rows
 from scaled_dot_product_08_amd import binding
 
 pytestmark = pytest.mark.gpu
 
 
-def run_padded(qb, kb, vb, dtype, causal, scale, with_lse=True):
+def run_padded(qb, kb, vb, dtype, causal, scale, with_lse=True, tile_rows=0):
     q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
-    o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, with_lse=with_lse)
+    o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, with_lse=with_lse,
+                         tile_rows=tile_rows)
     torch.cuda.synchronize()
     return o, lse
 
 
-def check_full(qb, kb, vb, dtype, causal, scale, cu=None):
-    """Whole-output comparison (small shapes)."""
+def check_full(qb, kb, vb, dtype, causal, scale, cu=None, tile_rows=0, case=None):
+    """Whole-output comparison (small shapes); ``case`` names the recorded margins."""
     qf, kf, vf = (synth.bits_to_f64(x, dtype) for x in (qb, kb, vb))
     if cu is None:
-        o, lse = run_padded(qb, kb, vb, dtype, causal, scale)
+        o, lse = run_padded(qb, kb, vb, dtype, causal, scale, tile_rows=tile_rows)
         oref, lref = attention(qf, kf, vf, causal=causal, scale=scale)
     else:
         q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
         cud = torch.from_numpy(cu).cuda()
-        o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cud)
+        o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cud,
+                             tile_rows=tile_rows)
         torch.cuda.synchronize()
         oref, lref = attention(qf, kf, vf, causal=causal, scale=scale, cu_seqlens=cu)
     eo, el = max_abs(to_f64(o), oref), max_abs(lse.cpu().numpy(), lref)
     say(f"    max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    if case is not None:
+        record(case, dtype, eo, el, oref=oref, n_rows=int(np.prod(oref.shape[:-1])))
     assert eo <= TOL_O[dtype], eo
     assert el <= TOL_LSE, el
     return eo, el
@@ -47,7 +51,8 @@ def test_config_tiny():
     cfg = synth.CONFIGS["tiny"]
     say("tiny", cfg.describe())
     inp = synth.make_inputs(cfg)
-    check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
+    check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D),
+               case="tiny " + cfg.describe() + " (every output)")
 
 
 @pytest.mark.parametrize("name", ["mha", "mha_causal"])
@@ -55,16 +60,18 @@ def test_config_mha_full(name):
     cfg = synth.CONFIGS[name]
     say(name, cfg.describe())
     inp = synth.make_inputs(cfg)
-    check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
+    check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D),
+               case=name + " " + cfg.describe() + " (every output)")
 
 
-def _sampled_padded(cfg, rows_per_head, heads_stride=1, seed_off=2):
+def _sampled_padded(cfg, rows_per_head, heads_stride=1, seed_off=2, case=None):
     inp = synth.make_inputs(cfg)
     scale = scale_of(cfg.D)
     o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale)
     o = o.cpu()
     lse = lse.cpu().numpy()
-    worst_o = worst_l = 0.0
+    worst_o = worst_l = floor = 0.0
+    n_rows = 0
     for b in range(cfg.B):
         rows = synth.sampled_rows(cfg.S, rows_per_head, cfg.seed + seed_off + b)
         heads = list(range(0, cfg.H, heads_stride))
@@ -73,22 +80,30 @@ def _sampled_padded(cfg, rows_per_head, heads_stride=1, seed_off=2):
         og = o[b][rows][:, heads].float().numpy().astype(np.float64)
         worst_o = max(worst_o, max_abs(og, oref))
         worst_l = max(worst_l, max_abs(lse[b][heads][:, rows], lref))
-    say(f"    sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+        floor = max(floor, rne_floor(oref, cfg.dtype))
+        n_rows += len(rows) * len(heads)
+    say(f"    sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e} ({n_rows} rows)")
+    if case is not None:
+        record(case, cfg.dtype, worst_o, worst_l, floor=floor, n_rows=n_rows)
     assert worst_o <= TOL_O[cfg.dtype]
     assert worst_l <= TOL_LSE
     assert torch.isfinite(o.float()).all()
 
 
 def test_config_llama_sampled():
+    """256 sampled query rows of every (batch, head) of the LLaMA-shaped layer, each against
+    all the keys it sees."""
     cfg = synth.CONFIGS["llama"]
     say("llama", cfg.describe())
-    _sampled_padded(cfg, rows_per_head=64)
+    _sampled_padded(cfg, rows_per_head=256,
+                    case="llama " + cfg.describe() + " (256 sampled rows of every (b, h))")
 
 
 def test_config_long_sampled():
     cfg = synth.CONFIGS["long"]
     say("long", cfg.describe())
-    _sampled_padded(cfg, rows_per_head=cfg.sample_rows, heads_stride=1)
+    _sampled_padded(cfg, rows_per_head=cfg.sample_rows, heads_stride=1,
+                    case=f"long {cfg.describe()} ({cfg.sample_rows} sampled rows of every head)")
 
 
 def test_config_varlen_sampled():
@@ -103,35 +118,26 @@ def test_config_varlen_sampled():
     o = o.cpu()
     lse = lse.cpu().numpy()
     say(f"    {len(cu) - 1} segments, lengths {np.diff(cu).tolist()}")
-    worst_o = worst_l = 0.0
+    worst_o = worst_l = floor = 0.0
+    n_rows = 0
+    heads = list(range(cfg.H))
     for s in range(len(cu) - 1):
         a, e = int(cu[s]), int(cu[s + 1])
         L = e - a
-        rows = synth.sampled_rows(L, min(L, 24), cfg.seed + 2 + s)
+        rows = synth.sampled_rows(L, min(L, 64), cfg.seed + 2 + s)
         qf, kf, vf = (synth.bits_to_f64(x[a:e], cfg.dtype) for x in (inp.q, inp.k, inp.v))
-        heads = [0, 7, 31]
         oref, lref = attention_rows(qf, kf, vf, rows, causal=True, scale=scale, heads=heads)
         og = o[a:e][rows][:, heads].float().numpy().astype(np.float64)
         worst_o = max(worst_o, max_abs(og, oref))
         worst_l = max(worst_l, max_abs(lse[heads][:, a + rows], lref))
-    say(f"    sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+        floor = max(floor, rne_floor(oref, cfg.dtype))
+        n_rows += len(rows) * len(heads)
+    say(f"    sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e} ({n_rows} rows)")
+    record(f"varlen {cfg.describe()} (64 sampled rows of every sequence, all {cfg.H} heads)",
+           cfg.dtype, worst_o, worst_l, floor=floor, n_rows=n_rows)
     assert worst_o <= TOL_O[cfg.dtype]
     assert worst_l <= TOL_LSE
     assert torch.isfinite(o.float()).all()
-
-
-@pytest.mark.parametrize("name", ["mha", "mha_causal", "llama", "long"])
-def test_config_64_row_waves(name, monkeypatch):
-    """The opt-in 64-row-wave kernel at the benchmark sizes: whole outputs for B4 H12 S2048 D64,
-    sampled rows of the LLaMA-shaped layer and of the 64K-token sequence."""
-    monkeypatch.setenv("ATTN_WAVES", "w64")
-    cfg = synth.CONFIGS[name]
-    say(name, "64-row waves", cfg.describe())
-    if name.startswith("mha"):
-        inp = synth.make_inputs(cfg)
-        check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
-    else:
-        _sampled_padded(cfg, rows_per_head=32 if name == "llama" else 48)
 
 
 # ---- reduced shapes: every tile boundary, ragged tails, both dtypes / D ----------
@@ -142,11 +148,9 @@ SHAPES = [
 ]
 
 
-@pytest.fixture(params=["4", "8", "w64"], ids=["bm128", "bm256", "bm256w64"])
-def waves(request, monkeypatch):
-    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles, and with the
-    256-row tiles of four 64-row waves."""
-    monkeypatch.setenv("ATTN_WAVES", request.param)
+@pytest.fixture(params=[128, 256], ids=["bm128", "bm256"])
+def tile_rows(request):
+    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles."""
     return request.param
 
 
@@ -154,22 +158,22 @@ def waves(request, monkeypatch):
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,S", SHAPES)
-def test_padded_shapes(B, H, S, D, dtype, causal, waves):
-    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal} waves={waves}")
+def test_padded_shapes(B, H, S, D, dtype, causal, tile_rows):
+    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal} tile_rows={tile_rows}")
     qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 1000 + S + D)
-    check_full(qb, kb, vb, dtype, causal, scale_of(D))
+    check_full(qb, kb, vb, dtype, causal, scale_of(D), tile_rows=tile_rows)
 
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_packed_shapes(D, dtype, causal, waves):
+def test_packed_shapes(D, dtype, causal, tile_rows):
     lens = [1, 3, 0, 130, 257, 64, 0, 128, 200, 513]
     cu = synth.cu_seqlens_of(lens)
     T = int(cu[-1])
-    say(f"packed lens={lens} D={D} {dtype} causal={causal}")
+    say(f"packed lens={lens} D={D} {dtype} causal={causal} tile_rows={tile_rows}")
     qb, kb, vb = synth.normal_qkv((T, 3, D), dtype, 77 + D)
-    check_full(qb, kb, vb, dtype, causal, scale_of(D), cu=cu)
+    check_full(qb, kb, vb, dtype, causal, scale_of(D), cu=cu, tile_rows=tile_rows)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9, 3.0])
@@ -189,7 +193,7 @@ def test_lse_optional():
 
 
 @pytest.mark.parametrize("name", ["llama", "mha_causal"])
-def test_tile_size_choice(name, monkeypatch):
+def test_tile_size_choice(name):
     """128- and 256-row query tiles: bitwise identical O and LSE for D = 128 (same per-row
     arithmetic over the same 64-key tiles). For D = 64 the 4-wave kernel walks 128-key tiles,
     so the lazy maximum and the fp16 row sums are grouped differently: each result is within
@@ -198,9 +202,9 @@ def test_tile_size_choice(name, monkeypatch):
     cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg, B=2 if cfg.B > 2 else cfg.B)
     outs = []
-    for w in ("4", "8"):
-        monkeypatch.setenv("ATTN_WAVES", w)
-        o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D))
+    for rows in (128, 256):
+        o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D),
+                            tile_rows=rows)
         outs.append((o.cpu(), lse.cpu()))
     if cfg.D == 128:
         assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

@@ -72,3 +72,22 @@ def test_rows_entry_matches_full(causal):
     orow, lrow = attention_rows(q[0], k[0], v[0], rows, causal=causal, scale=scale, heads=[0, 2])
     np.testing.assert_allclose(orow, o[0][rows][:, [0, 2]], rtol=0, atol=1e-13)
     np.testing.assert_allclose(lrow, lse[0][[0, 2]][:, rows], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window,n_global,alibi", [(16, 0, False), (0, 5, False), (0, 0, True),
+                                                   (24, 3, True), (1, 0, False), (500, 0, True)])
+def test_rows_entry_matches_full_with_masks(causal, window, n_global, alibi):
+    """attention_rows with the window, global-row and ALiBi variants equals the full oracle's
+    rows (the full oracle's variants are pinned by brute force in test_oracle_masks.py)."""
+    q, k, v = (synth.bits_to_f64(x, "bf16") for x in synth.normal_qkv((1, 230, 4, 64), "bf16", 18))
+    scale = 0.125
+    slopes = synth.alibi_slopes(4) if alibi else None
+    o, lse = attention(q, k, v, causal=causal, scale=scale, window=window, n_global=n_global,
+                       alibi_slopes=slopes)
+    rows = np.array([0, 1, 2, 4, 5, 6, 63, 64, 127, 128, 200, 229])
+    heads = [0, 3, 1]
+    orow, lrow = attention_rows(q[0], k[0], v[0], rows, causal=causal, scale=scale, heads=heads,
+                                window=window, n_global=n_global, alibi_slopes=slopes)
+    np.testing.assert_allclose(orow, o[0][rows][:, heads], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lrow, lse[0][heads][:, rows], rtol=0, atol=1e-13)
