@@ -42,7 +42,8 @@ enum {
   ATTN_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
   ATTN_ERR_SEQLENS = -7,     /* cu_seqlens failed validation (debug check) */
   ATTN_ERR_ALIGN = -8,       /* a tensor pointer is not 16-byte aligned */
-  ATTN_ERR_WORKSPACE = -9    /* attn_decode / attn_bwd: workspace NULL or too small */
+  ATTN_ERR_WORKSPACE = -9,   /* attn_decode / attn_bwd: workspace NULL or too small */
+  ATTN_ERR_SCRATCH = -10     /* attn_decode_noalloc: explicit split count beyond its scratch */
 };
 
 /*
@@ -191,6 +192,31 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
                 int S_max, int D, int causal, float scale, int dtype, int num_splits,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. It takes no workspace; the split partials live in a
+ * fixed array of the library, 16 MiB per GPU, which each GPU that runs this
+ * call holds until the process ends. The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks up
+ * that device's array address once (hipGetSymbolAddress).
+ *
+ * Arguments, layouts, semantics and results as attn_decode, without
+ * workspace / workspace_bytes. num_splits = 0 chooses the split count as
+ * attn_decode does and, when the partials of that choice would not fit in
+ * the array ((D + 1) * 4 bytes per split per query row), uses the largest
+ * count that fits (a single split needs none); an explicit num_splits whose
+ * partials do not fit returns ATTN_ERR_SCRATCH with nothing enqueued.
+ * Nothing in the array needs clearing: every call writes each partial it
+ * later reads. Calls on one GPU share its array, so calls that can overlap on
+ * one GPU (different streams, or another thread between enqueue and
+ * completion) race and give wrong results: order them on one stream.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                        int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                        void* stream);
 
 /*
  * attn_bwd -- gradients of attn_fwd with respect to q, k and v.

@@ -17,9 +17,10 @@ STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
     -4: "ATTN_ERR_SCALE", -5: "ATTN_ERR_UNSUPPORTED", -6: "ATTN_ERR_LAUNCH",
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
+    -10: "ATTN_ERR_SCRATCH",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
-           "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
+           "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -64,6 +65,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_decode.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
          ctypes.c_void_p]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -115,6 +119,15 @@ def attn_decode_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq
                                       int(H), int(Sq), int(S_max), int(D), int(causal),
                                       float(scale), int(dtype), int(num_splits), ws_ptr,
                                       int(ws_bytes), stream_ptr)
+
+
+def attn_decode_noalloc_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq, S_max, D,
+                            causal, scale, dtype, num_splits, stream_ptr) -> int:
+    """Direct call of attn_decode_noalloc with integer pointers; returns the status code."""
+    return load_library().attn_decode_noalloc(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr,
+                                              int(B), int(H), int(Sq), int(S_max), int(D),
+                                              int(causal), float(scale), int(dtype),
+                                              int(num_splits), stream_ptr)
 
 
 def attn_fwd_fp8_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dq, dk, dv,
@@ -275,12 +288,13 @@ def check_cu_seqlens(cu_seqlens, T: int, stream=None) -> int:
 
 def attn_decode(q, k_cache, v_cache, out, lse=None, *, seqlens_k=None, causal: bool = False,
                 scale: float | None = None, num_splits: int = 0, workspace=None,
-                stream=None) -> None:
+                stream=None, noalloc: bool = False) -> None:
     """Call attn_decode on torch device tensors.
 
     q, out (B, Sq, H, D); k_cache, v_cache (B, H, S_max, D); seqlens_k int32 (B,) or None;
     lse (B, H, Sq) fp32 or None; workspace a device tensor of at least
-    decode_workspace_size(...) bytes (allocated here with torch when None).
+    decode_workspace_size(...) bytes (allocated here with torch when None). With
+    ``noalloc`` it calls attn_decode_noalloc instead (no workspace; nothing allocated).
     """
     import torch
     _check_tensors(("q", "out"), (q, out))
@@ -298,6 +312,17 @@ def attn_decode(q, k_cache, v_cache, out, lse=None, *, seqlens_k=None, causal: b
         raise ValueError("seqlens_k must be an int32 tensor of B lengths on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("attn_decode_noalloc takes no workspace")
+        st = attn_decode_noalloc_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     None if seqlens_k is None else seqlens_k.data_ptr(),
+                                     out.data_ptr(), None if lse is None else lse.data_ptr(), B, H,
+                                     Sq, S_max, D, int(bool(causal)), scale, _dtype_code(q),
+                                     num_splits, _stream_ptr(stream))
+        if st != 0:
+            raise AttnError(st, attn_strerror(st))
+        return
     need = decode_workspace_size(B, H, Sq, S_max, D, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

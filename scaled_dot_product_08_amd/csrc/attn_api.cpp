@@ -107,6 +107,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_SEQLENS: return "cu_seqlens is not a valid prefix-offset array";
     case ATTN_ERR_ALIGN: return "tensor pointer misaligned (q/k/v/out need 16 bytes, lse 4)";
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_size";
+    case ATTN_ERR_SCRATCH:
+      return "the requested split count needs more than the library's 16 MiB per-GPU scratch array";
     default: return "unknown status";
   }
 }
@@ -209,20 +211,41 @@ size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int nu
   return decode_workspace_bytes((long long)B * H * Sq, plan, D);
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
-                int S_max, int D, int causal, float scale, int dtype, int num_splits,
-                void* workspace, size_t workspace_bytes, void* stream) {
+// Shared by attn_decode (caller's workspace) and attn_decode_noalloc (the
+// library's per-GPU scratch array; ws == nullptr and noalloc set).
+static int decode_common(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                         int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                         void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   sdpa08::DecodePlan plan{1, 0};
+  const bool ragged = seqlens_k != nullptr;
   const int st = validate_decode(q, k_cache, v_cache, out, lse, B, H, Sq, S_max, D, scale, dtype,
-                                 num_splits, seqlens_k != nullptr, &plan);
+                                 num_splits, ragged, &plan);
   if (st != ATTN_OK) return st;
   if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return ATTN_ERR_ALIGN;
   const long long rows = (long long)B * H * Sq;
-  const size_t need = decode_workspace_bytes(rows, plan, D);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  size_t need = decode_workspace_bytes(rows, plan, D);
+  if (noalloc && need > sdpa08::kDecodeScratchBytes) {
+    // An explicit split count is honoured or refused; the automatic choice
+    // shrinks to what the scratch array holds (one split needs none).
+    if (num_splits > 0) return ATTN_ERR_SCRATCH;
+    const long long per_split = rows * (long long)(D + 1) * (long long)sizeof(float);
+    long long fit = (long long)sdpa08::kDecodeScratchBytes / per_split;
+    if (fit < 1) fit = 1;
+    plan = sdpa08::decode_plan(B, H, Sq, S_max, D, (int)fit, ragged);
+    need = decode_workspace_bytes(rows, plan, D);
+    if (need > sdpa08::kDecodeScratchBytes) return ATTN_ERR_SCRATCH;   // cannot happen
+  }
+  if (!noalloc) {
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  }
   if (rows == 0) return ATTN_OK;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  float* part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  if (noalloc && need > 0) {
+    if (sdpa08::decode_scratch(hs, &part) != hipSuccess) return ATTN_ERR_LAUNCH;
+  }
   sdpa08::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
@@ -230,7 +253,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   p.seqlens = seqlens_k;
   p.o = static_cast<uint16_t*>(out);
   p.lse = lse;
-  p.part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  p.part_o = part;
   p.part_lse = need > 0 ? p.part_o + (size_t)rows * plan.n_splits * D : nullptr;
   p.B = B;
   p.H = H;
@@ -240,9 +263,24 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache,
   p.chunk = plan.chunk;
   p.c_log2 = scale * 1.4426950408889634f;
   p.causal = causal != 0;
-  const hipError_t e = sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16,
-                                             reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16, hs);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(q, k_cache, v_cache, seqlens_k, out, lse, B, H, Sq, S_max, D, causal,
+                       scale, dtype, num_splits, workspace, workspace_bytes, false, stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seqlens_k, void* out, float* lse, int B, int H, int Sq,
+                        int S_max, int D, int causal, float scale, int dtype, int num_splits,
+                        void* stream) {
+  return decode_common(q, k_cache, v_cache, seqlens_k, out, lse, B, H, Sq, S_max, D, causal,
+                       scale, dtype, num_splits, nullptr, 0, true, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int H, int S, int packed) {

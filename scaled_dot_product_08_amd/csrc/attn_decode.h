@@ -35,4 +35,13 @@ DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_re
 
 hipError_t launch_decode(const DecodeParams& p, int D, bool bf16, hipStream_t stream);
 
+// Size of the library's own per-GPU scratch array that attn_decode_noalloc
+// keeps the split partials in (instead of a caller's workspace).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+
+// Device address of that array on the device `stream` belongs to (the current
+// device for the null stream). The first call on a device looks it up with
+// that device current and keeps it; later calls return the kept address.
+hipError_t decode_scratch(hipStream_t stream, float** ptr);
+
 }  // namespace sdpa08

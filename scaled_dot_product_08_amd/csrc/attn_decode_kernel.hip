@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_decode.h"
 #include "gfx950_util.h"
 
@@ -307,6 +309,45 @@ DecodePlan decode_plan(int B, int H, int Sq, int S_max, int D, int num_splits_re
   n = ((long long)S_max + chunk - 1) / chunk;
   if (n < 1) n = 1;
   return DecodePlan{(int)n, (int)chunk};
+}
+
+// The split partials of attn_decode_noalloc: one array per GPU (each device
+// holds its own copy at its own address), kept until the process ends. In host
+// code `scratch` names a host-side stand-in, never a device address: kernels
+// get the address decode_scratch looked up.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const int current = dev;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != current && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (dev != current) {
+      const hipError_t e2 = hipSetDevice(current);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<float*>(a);
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int D, bool bf16, hipStream_t stream) {

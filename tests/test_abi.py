@@ -211,3 +211,27 @@ def test_binding_rejects_mismatched_tensors():
         binding.fwd_fp8(q, q, q, causal=False)
     with pytest.raises(ValueError):
         binding.attn_decode(q, q, q, q)
+
+
+def call_dec_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, sl=None, o=P, lse=None, B=2, H=4, Sq=1, S_max=4096, D=128, causal=0,
+             scale=0.1, dtype=binding.ATTN_DTYPE_BF16, ns=0)
+    a.update(kw)
+    return binding.attn_decode_noalloc_raw(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"],
+                                           a["B"], a["H"], a["Sq"], a["S_max"], a["D"],
+                                           a["causal"], a["scale"], a["dtype"], a["ns"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(D=96), -5), (dict(dtype=7), -3), (dict(scale=float("nan")), -4),
+    (dict(H=0), -2), (dict(ns=-1), -2), (dict(sl=P + 2), -8), (dict(o=P + 4), -8),
+    # 8192 query rows x 64 explicit splits x 129 floats: 270 MB of partials > 16 MiB
+    (dict(B=64, H=32, Sq=4, S_max=8192, ns=64), -10),
+])
+def test_decode_noalloc_argument_errors(kw, code):
+    assert call_dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_empty_problem_is_noop():
+    assert call_dec_noalloc(B=0) == 0
+    assert call_dec_noalloc(Sq=0, ns=3) == 0
