@@ -262,6 +262,15 @@ int attn_check_cu_seqlens(const int32_t* cu_seqlens, int B, int T, void* stream)
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int attn_version(void);
 
+/*
+ * The hipError_t of the most recent kernel launch (or device look-up) of
+ * any attn_* call on the calling thread: 0 after a successful launch, the
+ * runtime's code after one that returned ATTN_ERR_LAUNCH. Launches first clear
+ * an error that an earlier runtime call of the thread left pending, so the
+ * code is the launch's own.
+ */
+int attn_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

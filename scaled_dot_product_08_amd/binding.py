@@ -20,7 +20,8 @@ STATUS = {
     -10: "ATTN_ERR_SCRATCH",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
-           "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version")
+           "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version",
+           "attn_last_hip_error")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -28,8 +29,13 @@ _lib = None
 
 class AttnError(RuntimeError):
     def __init__(self, status: int, text: str):
+        hip = None
+        if status == -6 and _lib is not None:
+            hip = int(_lib.attn_last_hip_error())
+            text = f"{text} (hipError_t {hip})"
         super().__init__(f"{STATUS.get(status, status)}: {text}")
         self.status = status
+        self.hip_error = hip
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -41,6 +47,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     if not os.path.exists(p):
         raise RuntimeError(f"HIP attention library not built: {p} "
                            "(run python -m scaled_dot_product_08_amd.build)")
+    # One HIP runtime per process. torch bundles its own libamdhip64 under the same soname;
+    # loaded first, it also serves this library. Loading this library first would bring the
+    # system runtime in beside torch's, and of two runtimes in one process one sees no device
+    # (its launches fail with hipErrorNoDevice).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
@@ -76,6 +87,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_check_cu_seqlens.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_version.restype = ctypes.c_int
     lib.attn_version.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    lib.attn_last_hip_error.argtypes = []
     if path is None:
         _lib = lib
     return lib

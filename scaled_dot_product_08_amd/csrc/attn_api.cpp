@@ -32,6 +32,18 @@ bool debug_enabled() {
   return on;
 }
 
+// The HIP error of this thread's most recent launch (attn_last_hip_error).
+thread_local int g_last_hip_error = 0;
+
+// A stale error that an earlier runtime call of the caller's thread left
+// behind would otherwise be read back as this call's launch error.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int launch_status(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 // Validation shared by attn_fwd; no HIP call. Fills the grid size on success.
 int validate(const void* q, const void* k, const void* v, void* out, const float* lse, int B,
              int H, int S, int D, float scale, int dtype, const int32_t* cu, long long* grid) {
@@ -94,6 +106,8 @@ size_t decode_workspace_bytes(long long rows, const sdpa08::DecodePlan& plan, in
 extern "C" {
 
 int attn_version(void) { return kVersion; }
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
 
 const char* attn_strerror(int status) {
   switch (status) {
@@ -170,9 +184,9 @@ static int fwd_common(const void* q, const void* k, const void* v, void* out, fl
   p.window = window;
   p.n_global = n_global;
   p.alibi = alibi;
-  const hipError_t e = sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
-                                          tuning, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  clear_stale_error();
+  return launch_status(sdpa08::launch_fwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
+                                          tuning, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
@@ -244,7 +258,9 @@ static int decode_common(const void* q, const void* k_cache, const void* v_cache
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   float* part = need > 0 ? static_cast<float*>(workspace) : nullptr;
   if (noalloc && need > 0) {
-    if (sdpa08::decode_scratch(hs, &part) != hipSuccess) return ATTN_ERR_LAUNCH;
+    clear_stale_error();
+    const hipError_t es = sdpa08::decode_scratch(hs, &part);
+    if (es != hipSuccess) return launch_status(es);
   }
   sdpa08::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -263,8 +279,8 @@ static int decode_common(const void* q, const void* k_cache, const void* v_cache
   p.chunk = plan.chunk;
   p.c_log2 = scale * 1.4426950408889634f;
   p.causal = causal != 0;
-  const hipError_t e = sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16, hs);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  clear_stale_error();
+  return launch_status(sdpa08::launch_decode(p, D, dtype == ATTN_DTYPE_BF16, hs));
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -332,9 +348,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
   p.n_tiles = 0;
   p.c_log2 = scale * 1.4426950408889634f;
   p.scale = scale;
-  const hipError_t e = sdpa08::launch_bwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
-                                          reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  clear_stale_error();
+  return launch_status(sdpa08::launch_bwd(p, D, dtype == ATTN_DTYPE_BF16, causal != 0, packed,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -378,9 +394,9 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* 
     p.q_mode = 2;
   }
   p.v_descale = descale_v;
-  const hipError_t e = sdpa08::launch_fwd_fp8(p, out_dtype == ATTN_DTYPE_BF16, causal != 0, packed,
-                                              reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  clear_stale_error();
+  return launch_status(sdpa08::launch_fwd_fp8(p, out_dtype == ATTN_DTYPE_BF16, causal != 0,
+                                              packed, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -235,3 +235,11 @@ def test_decode_noalloc_argument_errors(kw, code):
 def test_decode_noalloc_empty_problem_is_noop():
     assert call_dec_noalloc(B=0) == 0
     assert call_dec_noalloc(Sq=0, ns=3) == 0
+
+
+def test_one_hip_runtime_in_the_process(lib):
+    """Loading the library through the binding leaves exactly one HIP runtime in the process
+    (torch's, which the library's dependency then resolves to)."""
+    maps = open("/proc/self/maps").read()
+    hips = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hips) == 1, hips
