@@ -200,7 +200,7 @@ def timed(step, steps: int, warmup: int, settle_ms: float, stream):
 
 
 def time_workload(cfg, steps: int, warmup: int, samples: int = 0, settle_ms: float = 0.0,
-                  tile_rows: int = 0, head_group: int = 0):
+                  tile_rows: int = 0, key_split: int = 0, head_group: int = 0):
     """Mean over ``steps`` back-to-back launches bracketed by events (after ``warmup``
     launches and a settle phase of ``settle_ms``); with ``samples``, also that many
     individually timed launches afterwards (median and minimum)."""
@@ -232,7 +232,8 @@ def time_workload(cfg, steps: int, warmup: int, samples: int = 0, settle_ms: flo
     def step():
         binding.attn_fwd(q, k, v, out, lse, causal=cfg.causal, scale=scale, cu_seqlens=cu,
                          stream=stream, window=cfg.window, n_global=cfg.n_global,
-                         alibi_slopes=slopes, tile_rows=tile_rows, head_group=head_group)
+                         alibi_slopes=slopes, tile_rows=tile_rows, key_split=key_split,
+                         head_group=head_group)
 
     ms, st, clk = timed(step, steps, warmup, settle_ms, stream)
     res = {"ms": ms, "flops": fl, "bytes": nbytes, "tflops": fl / (ms * 1e-3) / 1e12,
@@ -541,10 +542,12 @@ def side(args, synth):
     else:
         c = synth.CONFIGS[name]
         r2 = time_workload(c, args.steps, args.warmup, settle_ms=args.settle_ms,
-                           tile_rows=args.tile_rows, head_group=args.head_group)
+                           tile_rows=args.tile_rows, key_split=args.key_split,
+                           head_group=args.head_group)
         r = {"workload": c.describe(), "us_per_call": round(r2["ms"] * 1e3, 2),
              "tflops": round(r2["tflops"], 1), "frac_of_peak": round(r2["tflops"] / PEAK_TFLOPS, 4),
-             "tile_rows": args.tile_rows, "head_group": args.head_group,
+             "tile_rows": args.tile_rows, "key_split": args.key_split,
+             "head_group": args.head_group,
              "settle": r2["settle"], "clock": r2["clock"]}
     log(f"  {name}: {r}")
     calibration_copy(args.calib_copy_mib)
@@ -578,6 +581,7 @@ def main():
                     help="time only this side figure (a key of synth.CONFIGS or synth.DECODE_CONFIGS) "
                          "and print it as one JSON line")
     ap.add_argument("--tile-rows", type=int, default=0, help="--side forward: 128 or 256 (0: auto)")
+    ap.add_argument("--key-split", type=int, default=0, help="--side forward: 1 or 2 wave groups per tile (0: auto)")
     ap.add_argument("--head-group", type=int, default=0, help="--side forward: heads per XCD group (0: auto)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")

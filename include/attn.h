@@ -98,16 +98,24 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  * Same arguments, layouts, semantics and errors as attn_fwd, plus:
  *   tile_rows  : query rows per workgroup, 128 or 256; 0 lets the library
  *                choose as attn_fwd does. Anything else: ATTN_ERR_UNSUPPORTED.
+ *   key_split  : 1: one wave per 32 query rows walks all of the tile's keys;
+ *                2: two groups of waves share the rows and take alternate key
+ *                blocks, their partial results merged at the end (128-row
+ *                tiles only); 0 lets the library choose. Other values, or 2
+ *                with 256-row tiles: ATTN_ERR_UNSUPPORTED.
  *   head_group : how many (batch, head) pairs one XCD interleaves the query
  *                tiles of (clamped to B*H, or H when packed); 0 lets the
  *                library choose. Negative: ATTN_ERR_SHAPE.
- * Results do not depend on head_group. They do not depend on tile_rows for
- * D = 128; for D = 64 the 128-row tiles walk 128 keys per step instead of
- * 64, so the sums are grouped differently and results differ by rounding.
+ * Results do not depend on head_group. The launch shapes sum the keys of a
+ * row in different groupings (D = 64 walks 128 keys per step with 4 waves on
+ * 128 rows, 64 with 256 rows; the key split adds two partial sums), so they
+ * agree to rounding, except that 128- and 256-row tiles without a key split
+ * are bitwise identical for D = 128.
  */
 int attn_fwd_tuned(const void* q, const void* k, const void* v, void* out, float* lse,
                    int B, int H, int S, int D, int causal, float scale, int dtype,
-                   const int32_t* cu_seqlens, int tile_rows, int head_group, void* stream);
+                   const int32_t* cu_seqlens, int tile_rows, int key_split, int head_group,
+                   void* stream);
 
 /*
  * attn_fwd_ext -- attn_fwd with the mask and bias variants.

@@ -58,7 +58,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_tuned.restype = ctypes.c_int
     lib.attn_fwd_tuned.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
-        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+         ctypes.c_void_p]
     lib.attn_fwd_ext.restype = ctypes.c_int
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
@@ -110,11 +111,12 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scal
 
 
 def attn_fwd_tuned_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
-                       cu_ptr, tile_rows, head_group, stream_ptr) -> int:
+                       cu_ptr, tile_rows, key_split, head_group, stream_ptr) -> int:
     """Direct call of attn_fwd_tuned with integer pointers; returns the status code."""
     return load_library().attn_fwd_tuned(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H),
                                          int(S), int(D), int(causal), float(scale), int(dtype),
-                                         cu_ptr, int(tile_rows), int(head_group), stream_ptr)
+                                         cu_ptr, int(tile_rows), int(key_split), int(head_group),
+                                         stream_ptr)
 
 
 def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
@@ -222,14 +224,16 @@ def _stream_ptr(stream):
 
 def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None,
              cu_seqlens=None, stream=None, window: int = 0, n_global: int = 0,
-             alibi_slopes=None, tile_rows: int = 0, head_group: int = 0) -> None:
+             alibi_slopes=None, tile_rows: int = 0, key_split: int = 0,
+             head_group: int = 0) -> None:
     """Call attn_fwd on torch device tensors.
 
     Padded: q,k,v,out (B,S,H,D), lse (B,H,S) fp32 or None.
     Packed: q,k,v,out (T,H,D), cu_seqlens int32 (nseq+1,), lse (H,T) or None.
     ``scale=None`` means 1/sqrt(D) rounded to float32. ``window``, ``n_global`` and
     ``alibi_slopes`` (float32 device tensor of H slopes) call attn_fwd_ext;
-    ``tile_rows`` / ``head_group`` (launch shape, 0 = automatic) call attn_fwd_tuned.
+    ``tile_rows`` / ``key_split`` / ``head_group`` (launch shape, 0 = automatic) call
+    attn_fwd_tuned.
     """
     _check_tensors(("q", "k", "v", "out"), (q, k, v, out))
     if cu_seqlens is None:
@@ -249,12 +253,13 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
         scale = 1.0 / math.sqrt(D)
     lse_ptr = None if lse is None else lse.data_ptr()
     masks = bool(window or n_global or alibi_slopes is not None)
-    if masks and (tile_rows or head_group):
+    tuned = bool(tile_rows or key_split or head_group)
+    if masks and tuned:
         raise ValueError("the mask/bias variants take no launch-shape arguments")
-    if tile_rows or head_group:
+    if tuned:
         st = attn_fwd_tuned_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                                 B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
-                                tile_rows, head_group, _stream_ptr(stream))
+                                tile_rows, key_split, head_group, _stream_ptr(stream))
     elif masks:
         al = None
         if alibi_slopes is not None:
@@ -276,7 +281,7 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
 
 def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
         with_lse: bool = True, stream=None, window: int = 0, n_global: int = 0,
-        alibi_slopes=None, tile_rows: int = 0, head_group: int = 0):
+        alibi_slopes=None, tile_rows: int = 0, key_split: int = 0, head_group: int = 0):
     """Allocate O (and LSE) with torch and run attn_fwd. Returns (O, LSE or None)."""
     import torch
     out = torch.empty_like(q)
@@ -290,7 +295,7 @@ def fwd(q, k, v, *, causal: bool, scale: float | None = None, cu_seqlens=None,
             lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, out, lse, causal=causal, scale=scale, cu_seqlens=cu_seqlens, stream=stream,
              window=window, n_global=n_global, alibi_slopes=alibi_slopes, tile_rows=tile_rows,
-             head_group=head_group)
+             key_split=key_split, head_group=head_group)
     return out, lse
 
 

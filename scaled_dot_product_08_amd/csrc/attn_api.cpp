@@ -198,11 +198,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 
 int attn_fwd_tuned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                    int H, int S, int D, int causal, float scale, int dtype,
-                   const int32_t* cu_seqlens, int tile_rows, int head_group, void* stream) {
+                   const int32_t* cu_seqlens, int tile_rows, int key_split, int head_group,
+                   void* stream) {
   if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256) return ATTN_ERR_UNSUPPORTED;
+  if (key_split < 0 || key_split > 2 || (key_split == 2 && tile_rows == 256)) {
+    return ATTN_ERR_UNSUPPORTED;
+  }
   if (head_group < 0) return ATTN_ERR_SHAPE;
   sdpa08::FwdTuning t;
   t.tile_rows = tile_rows;
+  t.key_split = key_split;
   t.head_group = head_group;
   return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, 0, 0,
                     nullptr, t, stream);

@@ -53,19 +53,29 @@ __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), one, acc, false);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT>
+// KS = 2: the waves form two groups that share the workgroup's query rows and
+// take alternate key blocks of every tile; the two partial results (running
+// maximum, row sum, accumulator) are merged through LDS at the end. It doubles
+// the waves per query tile, so problems with few tiles fill the chip in whole
+// rounds instead of leaving a half-empty last round.
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) {
   constexpr int NWAVES = NW;
-  constexpr int BM = 32 * NW;                  // query rows per workgroup
-  // Keys per LDS tile: 128 for D = 64 with 4 waves (the same 16 KB as 64 keys
-  // of D = 128, twice the matrix work per barrier and per softmax pass;
-  // measured 2-7 % faster on B4 H12 S2048, 7 % slower with 8 waves), else 64.
-  constexpr int BN = (D == 64 && !EXT && NW == 4) ? 128 : 64;
-  constexpr int NKB = BN / 32;                 // 32-key blocks per tile
+  constexpr int NWR = NW / KS;                 // waves per key group (one per 32 query rows)
+  constexpr int BM = 32 * NWR;                 // query rows per workgroup
+  // Keys per group block: 128 for D = 64 with 4 waves per group (the same
+  // 16 KB as 64 keys of D = 128, twice the matrix work per barrier and per
+  // softmax pass; measured 2-7 % faster on B4 H12 S2048, 7 % slower with 8
+  // waves on 256 rows), else 64.
+  constexpr int BN = (D == 64 && !EXT && NWR == 4) ? 128 : 64;
+  constexpr int GBN = KS * BN;                 // keys per LDS tile (all groups)
+  constexpr int NKB = BN / 32;                 // 32-key blocks per group block
   constexpr int ROWB = D * 2;                  // bytes per K/V row
-  constexpr int TILEB = BN * ROWB;             // bytes per K (or V) tile
-  constexpr int STAGEB = 2 * TILEB;            // K tile + V tile
-  constexpr int LDW = TILEB / 1024 / NWAVES;   // 1 KB direct loads per wave per tile
+  constexpr int TILEB = BN * ROWB;             // bytes of one group's K (or V) block
+  constexpr int GTILEB = GBN * ROWB;           // bytes per K (or V) tile
+  constexpr int STAGEB = 2 * GTILEB;           // K tile + V tile
+  constexpr int LDW = GTILEB / 1024 / NWAVES;  // 1 KB direct loads per wave per tile
+  static_assert(KS == 1 || (KS == 2 && !EXT), "key split: plain masks only");
   constexpr int DCH = D / 16;                  // 16-deep contraction chunks of Q K^T
   constexpr int DB = D / 32;                   // 32-row blocks of O^T
   static_assert(LDW >= 1, "tile must give every wave a 1 KB load");
@@ -81,6 +91,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   const int wave = tid >> 6;
   const int li = lane & 31;     // query row inside the wave / MFMA row index
   const int hh = lane >> 5;     // which half of the contraction this lane feeds
+  const int wr = KS == 1 ? wave : wave % NWR;   // which 32 query rows of the tile
+  const int kgrp = KS == 1 ? 0 : wave / NWR;    // which key block of every tile
 
   // ---- which (sequence, head, query tile) this workgroup owns -------------
   // Workgroup i runs on XCD i % 8. Undo that interleave so each XCD owns a
@@ -141,9 +153,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       if (!CAUSAL) kv_hi = min(L, q0 + BM - 1 + p.window);
     }
   }
-  const int j_lo = kv_lo / BN;
-  const int n_kv = (kv_hi + BN - 1) / BN;          // one past the last tile
-  const int wq0 = q0 + wave * 32;        // first query row of this wave
+  const int j_lo = kv_lo / GBN;
+  const int n_kv = (kv_hi + GBN - 1) / GBN;        // one past the last tile
+  const int wq0 = q0 + wr * 32;          // first query row of this wave
   const int qi = wq0 + li;               // this lane's query row
   // Mask-variant state of this wave (EXT only).
   const int win = EXT ? p.window : 0;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   // ---- Q^T operand, resident in registers for the whole key loop ----------
   // Rows past the sequence end read as zeros (buffer range check).
   const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(qg, q_rows * tok_bytes);
-  const uint32_t q_voff = (uint32_t)(wave * 32 + li) * tok_bytes + hh * 16;
+  const uint32_t q_voff = (uint32_t)(wr * 32 + li) * tok_bytes + hh * 16;
   // Sign handling of the scale: negative scale uses -Q and |scale|; zero
   // scale zeroes Q so every visible score is exactly 0.
   const uint32_t q_xor = (p.q_mode == 1) ? 0x80008000u : 0u;
@@ -206,12 +218,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 
   // Issue the direct loads of key tile j into stage `st`.
   auto issue_tile = [&](int j, int st) {
-    const int key0 = j * BN;
-    const uint32_t rows = (uint32_t)min(L - key0, BN);
+    const int key0 = j * GBN;
+    const uint32_t rows = (uint32_t)min(L - key0, GBN);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
     uint8_t* kdst = (st ? smem1 : smem0) + wave * LDW * 1024;
-    uint8_t* vdst = kdst + TILEB;
+    uint8_t* vdst = kdst + GTILEB;
 #pragma unroll
     for (int u = 0; u < LDW; ++u) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
@@ -229,9 +241,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   float m_run = -INFINITY;     // running max of the log2-scaled logits
   float l_run = 0.0f;          // this lane's half of the running exp-sum
 
-  auto compute_tile = [&](int j, const uint8_t* ks) {
-    const uint8_t* vs = ks + TILEB;
-    const int key0 = j * BN;
+  auto compute_tile = [&](int j, const uint8_t* stage) {
+    const uint8_t* ks = stage + kgrp * TILEB;
+    const uint8_t* vs = stage + GTILEB + kgrp * TILEB;
+    const int key0 = j * GBN + kgrp * BN;
     // A wave none of whose rows sees a key of this tile has nothing to do.
     if constexpr (EXT) {
       if (!w_any_glob) {
@@ -397,8 +410,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         m_run = m_new;
       }
       // A row that has seen no visible key yet keeps m = -inf (its scores here
-      // are all -inf too): subtract 0 instead, which gives exp2(-inf) = 0.
-      tile_l = exps((EXT && m_run == -INFINITY) ? 0.0f : m_run);
+      // are all -inf too): subtract 0 instead, which gives exp2(-inf) = 0. (Only
+      // with the mask variants or the key split can a wave's first tile hold
+      // rows that see none of its keys.)
+      tile_l = exps(((EXT || KS > 1) && m_run == -INFINITY) ? 0.0f : m_run);
     }
     l_run += tile_l;
 
@@ -438,12 +453,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     __syncthreads();
   }
 
+  if constexpr (KS == 2) {
+    // Merge the two key groups through LDS (the loop ended with every load
+    // done and every wave past its last barrier, so both stages are free).
+    // Group 0 saw key 0 of every row, so its running maximum is finite.
+    float* xa = reinterpret_cast<float*>(smem0);   // [NWR][DB][16][64] accumulators
+    float* xm = reinterpret_cast<float*>(smem1);   // [NWR][2][64] maximum and row sum
+    static_assert(NWR * DB * 16 * 64 * 4 <= STAGEB, "merge area");
+    if (kgrp == 1) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xa[((wr * DB + d) * 16 + r) * 64 + lane] = acc[d][r];
+      }
+      xm[(wr * 2 + 0) * 64 + lane] = m_run;
+      xm[(wr * 2 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kgrp == 1) return;
+    const float m1 = xm[(wr * 2 + 0) * 64 + lane];
+    const float l1 = xm[(wr * 2 + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[d][r] = fmaf(acc[d][r], a0, xa[((wr * DB + d) * 16 + r) * 64 + lane] * a1);
+      }
+    }
+    l_run = fmaf(l_run, a0, l1 * a1);
+    m_run = mm;
+  }
+
   // ---- epilogue: O = acc / l, LSE = ln(l) + m -------------------------------
   const float l_tot = half_sum(l_run);
   const float inv = 1.0f / l_tot;
   // Stores past the sequence end fall outside the descriptor and are dropped.
   const __amdgpu_buffer_rsrc_t o_rsrc = make_rsrc(og, q_rows * tok_bytes);
-  const uint32_t o_voff = (uint32_t)(wave * 32 + li) * tok_bytes + hh * 16;
+  const uint32_t o_voff = (uint32_t)(wr * 32 + li) * tok_bytes + hh * 16;
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -465,28 +514,44 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 }
 
 
-// Workgroup size: 8 waves (256 query rows, one workgroup per CU) when the
-// problem has enough 256-row tiles to fill the chip several times over; else
-// 4 waves (128 rows, two workgroups per CU), which balances small problems
-// better. Both share every per-row arithmetic step.
+// Workgroup shape by problem size (query tiles of 256 rows, 128-row tiles
+// counted per (batch, head) pair):
+//  * 8 waves on 256 rows (one workgroup per CU) when there are enough 256-row
+//    tiles to fill the chip several times over;
+//  * 8 waves on 128 rows with the keys of every tile split between two wave
+//    groups (KS = 2, one workgroup per CU) when the 128-row tiles fit in one
+//    round of the 256 CUs: twice the waves per tile (B1 H8 S4096 D128 causal,
+//    256 tiles: 55 us vs 71 us with 4 waves; B2 H4 S2048 D64, 128 tiles: 20 vs
+//    24 us). With more tiles the 4-wave shape is faster (B4 H12 S2048 D64, 768
+//    tiles: 60 vs 65 us; B1 H16 S8192 D128 causal, 1024 tiles: 255 vs 264 us);
+//  * else 4 waves on 128 rows (two workgroups per CU).
 constexpr long long kBigProblemTiles = 2048;
+constexpr long long kKeySplitMaxTiles = 256;
 
-static int choose_waves(const FwdParams& p, bool varlen) {
+enum class Shape { W4, W8, W8_KS2 };
+
+static Shape choose_shape(const FwdParams& p, bool varlen, const FwdTuning& t) {
+  if (t.tile_rows == 256) return Shape::W8;
+  if (t.tile_rows == 128) return t.key_split == 2 ? Shape::W8_KS2 : Shape::W4;
   const long long bh = varlen ? p.H : (long long)p.B * p.H;
   const long long tiles256 = varlen ? (long long)p.S / 256 + p.B : ((long long)p.S + 255) / 256;
-  return tiles256 * bh >= kBigProblemTiles ? 8 : 4;
+  const long long tiles128 = varlen ? (long long)p.S / 128 + p.B : ((long long)p.S + 127) / 128;
+  if (tiles256 * bh >= kBigProblemTiles) return Shape::W8;
+  if (t.key_split == 1) return Shape::W4;
+  if (t.key_split == 2 || tiles128 * bh <= kKeySplitMaxTiles) return Shape::W8_KS2;
+  return Shape::W4;
 }
 
 int max_query_tile_rows() { return 256; }
 int min_query_tile_rows() { return 128; }
 
-// Heads per XCD group for the plain 128-row tiles. Each XCD owns a contiguous
-// run of about nbh / 8 heads; when the K and V of that whole run fit in the
-// XCD's 4 MB L2, one group spans it, so the XCD starts the longest causal
-// tiles of all its heads first (B4 H12 S2048 D64: 6 heads of 0.5 MB, causal
-// +11 % over groups of 2 and +17 % over 4, non-causal unchanged; groups of 8,
-// which straddle XCDs, gained nothing). Otherwise groups of 2 (16 heads of
-// 2 MB measured clearly slower).
+// Heads per XCD group for 128-row tiles. Each XCD owns a contiguous run of
+// about nbh / 8 heads; when the K and V of that whole run fit in the XCD's
+// 4 MB L2, one group spans it, so the XCD starts the longest causal tiles of
+// all its heads first (B4 H12 S2048 D64: 6 heads of 0.5 MB, causal +11 % over
+// groups of 2 and +17 % over 4, non-causal unchanged; groups of 8, which
+// straddle XCDs, gained nothing). Otherwise groups of 2 (16 heads of 2 MB
+// measured clearly slower).
 static int head_group_128(const FwdParams& p, int D, bool varlen) {
   const long long nbh = varlen ? p.H : (long long)p.B * p.H;
   const long long per_xcd = (nbh + NXCD - 1) / NXCD;
@@ -497,16 +562,29 @@ static int head_group_128(const FwdParams& p, int D, bool varlen) {
   return g < 1 ? 1 : (int)g;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT>
+// Heads per XCD group for 256-row tiles: HEAD_GROUP, except for long padded
+// sequences whose K and V per head exceed 8 MB, where groups of 2 put more of
+// an XCD's concurrent workgroups on one head's K/V stream (B1 H32 S65536 D64
+// causal: 16.9 ms with groups of 2 or 1, 17.3 ms with 4, 22 ms with 8; the
+// LLaMA-shaped layer and the packed batch are fastest with 4).
+static int head_group_256(const FwdParams& p, int D, bool varlen) {
+  const long long kv_bytes_head = (long long)p.S * D * 2 * 2;
+  return (!varlen && kv_bytes_head > (8LL << 20)) ? 2 : HEAD_GROUP;
+}
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS>
 static hipError_t launch_one(FwdParams p, int head_group, hipStream_t stream) {
-  constexpr long long BM = 32 * NW;
+  constexpr long long BM = 32 * NW / KS;
   const long long tiles = VARLEN ? (long long)p.S / BM + p.B : ((long long)p.S + BM - 1) / BM;
   p.n_qtiles = (int)tiles;
   const long long nbh = VARLEN ? p.H : (long long)p.B * p.H;
-  if (head_group <= 0) head_group = (NW == 4 && !EXT) ? head_group_128(p, D, VARLEN) : HEAD_GROUP;
+  if (head_group <= 0) {
+    head_group = EXT ? HEAD_GROUP : BM == 128 ? head_group_128(p, D, VARLEN)
+                                              : head_group_256(p, D, VARLEN);
+  }
   p.head_group = (int)(head_group < nbh ? head_group : nbh);
-  const long long grid = tiles * (VARLEN ? p.H : (long long)p.B * p.H);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW, EXT>), dim3((unsigned)grid),
+  const long long grid = tiles * nbh;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW, EXT, KS>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -515,11 +593,14 @@ template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 static hipError_t launch_nw(const FwdParams& p, const FwdTuning& t, hipStream_t stream) {
   // The mask/bias variants run with 4-wave workgroups only.
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
-    return launch_one<D, BF16, CAUSAL, VARLEN, 4, true>(p, t.head_group, stream);
+    return launch_one<D, BF16, CAUSAL, VARLEN, 4, true, 1>(p, t.head_group, stream);
   }
-  const int w = t.tile_rows == 256 ? 8 : t.tile_rows == 128 ? 4 : choose_waves(p, VARLEN);
-  return w == 8 ? launch_one<D, BF16, CAUSAL, VARLEN, 8, false>(p, t.head_group, stream)
-                : launch_one<D, BF16, CAUSAL, VARLEN, 4, false>(p, t.head_group, stream);
+  switch (choose_shape(p, VARLEN, t)) {
+    case Shape::W8: return launch_one<D, BF16, CAUSAL, VARLEN, 8, false, 1>(p, t.head_group, stream);
+    case Shape::W8_KS2:
+      return launch_one<D, BF16, CAUSAL, VARLEN, 8, false, 2>(p, t.head_group, stream);
+    default: return launch_one<D, BF16, CAUSAL, VARLEN, 4, false, 1>(p, t.head_group, stream);
+  }
 }
 
 template <int D, bool BF16>

@@ -32,6 +32,7 @@ int min_query_tile_rows();
 struct FwdTuning {
   int tile_rows = 0;        // query rows per workgroup: 128 or 256
   int head_group = 0;       // heads whose query tiles one XCD interleaves
+  int key_split = 0;        // 1: one wave per 32 rows; 2: two wave groups split the keys (128-row tiles)
 };
 
 // Launch the kernel instance for (D, dtype, causal, packed) on `stream`; picks

@@ -69,19 +69,20 @@ def test_empty_problems_are_noops(kw):
     assert call(**kw) == 0
 
 
-def call_tuned(tile_rows=0, head_group=0, **kw):
+def call_tuned(tile_rows=0, head_group=0, key_split=0, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=2, S=128, D=64, causal=0, scale=0.125,
              dtype=binding.ATTN_DTYPE_FP16, cu=None)
     a.update(kw)
     return binding.attn_fwd_tuned_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
                                       a["S"], a["D"], a["causal"], a["scale"], a["dtype"], a["cu"],
-                                      tile_rows, head_group, None)
+                                      tile_rows, key_split, head_group, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(tile_rows=64), -5), (dict(tile_rows=-128), -5), (dict(tile_rows=512), -5),
     (dict(head_group=-1), -2), (dict(tile_rows=128, D=96), -5), (dict(head_group=3, q=None), -1),
     (dict(tile_rows=256, scale=float("nan")), -4), (dict(tile_rows=256, H=0), -2),
+    (dict(key_split=3), -5), (dict(key_split=-1), -5), (dict(tile_rows=256, key_split=2), -5),
 ])
 def test_tuned_argument_errors(kw, code):
     assert call_tuned(**kw) == code

@@ -14,23 +14,26 @@ pytestmark = pytest.mark.gpu
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
-@pytest.mark.parametrize("tile_rows", [128, 256])
+SHAPES = [(128, 1), (128, 2), (256, 1)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["bm128", "bm128ks2", "bm256"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_counts_and_constant_values_packed(D, dtype, causal, tile_rows):
+def test_counts_and_constant_values_packed(D, dtype, causal, shape):
     """Q=K=0: every visible key has weight 1, so exp(LSE) is the count of visible keys and
     O equals the per-sequence constant V bit for bit; any cross-sequence leak breaks both."""
     lens = [1, 5, 0, 64, 129, 300, 2, 1000, 77]
     cu = synth.cu_seqlens_of(lens)
     T, H = int(cu[-1]), 2
-    say(f"counts packed D={D} {dtype} causal={causal} tile_rows={tile_rows}")
+    say(f"counts packed D={D} {dtype} causal={causal} shape={shape}")
     q = torch.zeros((T, H, D), dtype=DT[dtype], device="cuda")
     k = torch.zeros_like(q)
     consts = np.repeat(np.arange(1, len(lens) + 1, dtype=np.float32), lens)
     v = torch.from_numpy(consts).to(DT[dtype]).cuda()[:, None, None].expand(T, H, D).contiguous()
     o, lse = binding.fwd(q, k, v, causal=causal, scale=0.125, cu_seqlens=torch.from_numpy(cu).cuda(),
-                         tile_rows=tile_rows)
+                         tile_rows=shape[0], key_split=shape[1])
     torch.cuda.synchronize()
     counts = np.rint(np.exp(lse.cpu().numpy().astype(np.float64))).astype(np.int64)
     expect = np.concatenate([np.arange(1, n + 1) if causal else np.full(n, n) for n in lens if n])
@@ -39,14 +42,16 @@ def test_counts_and_constant_values_packed(D, dtype, causal, tile_rows):
     np.testing.assert_array_equal(o.float().cpu().numpy(), v.float().cpu().numpy())
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=["bm128", "bm128ks2", "bm256"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_counts_padded(D):
+def test_counts_padded(D, shape):
     B, S, H = 2, 333, 3
     q = torch.zeros((B, S, H, D), dtype=torch.float16, device="cuda")
     k = torch.zeros_like(q)
     v = torch.ones_like(q) * 3
     for causal in (False, True):
-        o, lse = binding.fwd(q, k, v, causal=causal, scale=0.5)
+        o, lse = binding.fwd(q, k, v, causal=causal, scale=0.5, tile_rows=shape[0],
+                             key_split=shape[1])
         torch.cuda.synchronize()
         counts = np.rint(np.exp(lse.cpu().numpy().astype(np.float64))).astype(np.int64)
         expect = np.arange(1, S + 1) if causal else np.full(S, S)
@@ -54,12 +59,13 @@ def test_counts_padded(D):
         assert (o == 3).all()
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=["bm128", "bm128ks2", "bm256"])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_causal_row0_is_v0_bitwise(dtype, D):
+def test_causal_row0_is_v0_bitwise(dtype, D, shape):
     qb, kb, vb = synth.normal_qkv((2, 70, 3, D), dtype, 9)
     q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
-    o, lse = binding.fwd(q, k, v, causal=True, scale=0.3)
+    o, lse = binding.fwd(q, k, v, causal=True, scale=0.3, tile_rows=shape[0], key_split=shape[1])
     torch.cuda.synchronize()
     assert torch.equal(o[:, 0], v[:, 0])
 
@@ -74,9 +80,9 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("tile_rows", [128, 256])
+@pytest.mark.parametrize("wg", SHAPES, ids=["bm128", "bm128ks2", "bm256"])
 @pytest.mark.parametrize("packed", [False, True])
-def test_guard_bands_untouched(packed, tile_rows):
+def test_guard_bands_untouched(packed, wg):
     """Sentinel regions around out and lse stay intact (no writes past the tensors)."""
     G = 4096
     D, H = 128, 2
@@ -96,7 +102,8 @@ def test_guard_bands_untouched(packed, tile_rows):
     lbuf = torch.full((nl + 2 * G,), -7.0, dtype=torch.float32, device="cuda")
     out = obuf[G:G + n].view(shape)
     lse = lbuf[G:G + nl].view(lshape)
-    binding.attn_fwd(q, k, v, out, lse, causal=True, cu_seqlens=cu, tile_rows=tile_rows)
+    binding.attn_fwd(q, k, v, out, lse, causal=True, cu_seqlens=cu, tile_rows=wg[0],
+                     key_split=wg[1])
     torch.cuda.synchronize()
     assert (obuf[:G] == 7).all() and (obuf[G + n:] == 7).all()
     assert (lbuf[:G] == -7).all() and (lbuf[G + nl:] == -7).all()
@@ -141,9 +148,9 @@ def test_debug_validator_rejects_bad_offsets():
     assert "status -7" in r.stdout and "good ok" in r.stdout
 
 
-@pytest.mark.parametrize("tile_rows", [128, 256])
+@pytest.mark.parametrize("wg", SHAPES, ids=["bm128", "bm128ks2", "bm256"])
 @pytest.mark.parametrize("packed", [False, True])
-def test_head_group_does_not_change_results(packed, tile_rows):
+def test_head_group_does_not_change_results(packed, wg):
     """The XCD head grouping only reorders workgroups: O and LSE are bitwise identical for
     every group size, including sizes that do not divide the head count and ones above it."""
     D, H = 128, 7
@@ -158,7 +165,8 @@ def test_head_group_does_not_change_results(packed, tile_rows):
     q, k, v = (to_dev(x, "bf16") for x in (qb, kb, vb))
     ref = None
     for g in (1, 2, 3, 5, 7, 21, 1000):
-        o, lse = binding.fwd(q, k, v, causal=True, cu_seqlens=cu, tile_rows=tile_rows, head_group=g)
+        o, lse = binding.fwd(q, k, v, causal=True, cu_seqlens=cu, tile_rows=wg[0],
+                             key_split=wg[1], head_group=g)
         torch.cuda.synchronize()
         if ref is None:
             ref = (o.clone(), lse.clone())

@@ -47,7 +47,8 @@ def test_max_heads_d128_full_tiles(tile_rows):
         q[:, :, h] = to_dev(np.ascontiguousarray(qb[:, :, i]), "bf16")
         k[:, :, h] = to_dev(np.ascontiguousarray(kb[:, :, i]), "bf16")
         v[:, :, h] = to_dev(np.ascontiguousarray(vb[:, :, i]), "bf16")
-    o, lse = binding.fwd(q, k, v, causal=True, scale=scale_of(D), tile_rows=tile_rows)
+    o, lse = binding.fwd(q, k, v, causal=True, scale=scale_of(D), tile_rows=tile_rows,
+                         key_split=2 if tile_rows == 128 else 1)
     torch.cuda.synchronize()
     f = [synth.bits_to_f64(x, "bf16") for x in (qb, kb, vb)]
     oref, lref = attention(*f, causal=True, scale=scale_of(D))

@@ -15,25 +15,25 @@ from scaled_dot_product_08_amd import binding
 pytestmark = pytest.mark.gpu
 
 
-def run_padded(qb, kb, vb, dtype, causal, scale, with_lse=True, tile_rows=0):
+def run_padded(qb, kb, vb, dtype, causal, scale, with_lse=True, shape=(0, 0)):
     q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
     o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, with_lse=with_lse,
-                         tile_rows=tile_rows)
+                         tile_rows=shape[0], key_split=shape[1])
     torch.cuda.synchronize()
     return o, lse
 
 
-def check_full(qb, kb, vb, dtype, causal, scale, cu=None, tile_rows=0, case=None):
+def check_full(qb, kb, vb, dtype, causal, scale, cu=None, shape=(0, 0), case=None):
     """Whole-output comparison (small shapes); ``case`` names the recorded margins."""
     qf, kf, vf = (synth.bits_to_f64(x, dtype) for x in (qb, kb, vb))
     if cu is None:
-        o, lse = run_padded(qb, kb, vb, dtype, causal, scale, tile_rows=tile_rows)
+        o, lse = run_padded(qb, kb, vb, dtype, causal, scale, shape=shape)
         oref, lref = attention(qf, kf, vf, causal=causal, scale=scale)
     else:
         q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
         cud = torch.from_numpy(cu).cuda()
         o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cud,
-                             tile_rows=tile_rows)
+                             tile_rows=shape[0], key_split=shape[1])
         torch.cuda.synchronize()
         oref, lref = attention(qf, kf, vf, causal=causal, scale=scale, cu_seqlens=cu)
     eo, el = max_abs(to_f64(o), oref), max_abs(lse.cpu().numpy(), lref)
@@ -148,9 +148,14 @@ SHAPES = [
 ]
 
 
-@pytest.fixture(params=[128, 256], ids=["bm128", "bm256"])
-def tile_rows(request):
-    """Run the test with 128-row (4-wave) and 256-row (8-wave) query tiles."""
+SHAPE_PARAMS = [(128, 1), (128, 2), (256, 1)]
+SHAPE_IDS = ["bm128", "bm128ks2", "bm256"]
+
+
+@pytest.fixture(params=SHAPE_PARAMS, ids=SHAPE_IDS)
+def shape(request):
+    """Run the test with each workgroup shape: 128-row tiles (4 waves), 128-row tiles whose
+    keys two groups of 4 waves split, and 256-row tiles (8 waves)."""
     return request.param
 
 
@@ -158,22 +163,22 @@ def tile_rows(request):
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,H,S", SHAPES)
-def test_padded_shapes(B, H, S, D, dtype, causal, tile_rows):
-    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal} tile_rows={tile_rows}")
+def test_padded_shapes(B, H, S, D, dtype, causal, shape):
+    say(f"padded B={B} H={H} S={S} D={D} {dtype} causal={causal} shape={shape}")
     qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 1000 + S + D)
-    check_full(qb, kb, vb, dtype, causal, scale_of(D), tile_rows=tile_rows)
+    check_full(qb, kb, vb, dtype, causal, scale_of(D), shape=shape)
 
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_packed_shapes(D, dtype, causal, tile_rows):
+def test_packed_shapes(D, dtype, causal, shape):
     lens = [1, 3, 0, 130, 257, 64, 0, 128, 200, 513]
     cu = synth.cu_seqlens_of(lens)
     T = int(cu[-1])
-    say(f"packed lens={lens} D={D} {dtype} causal={causal} tile_rows={tile_rows}")
+    say(f"packed lens={lens} D={D} {dtype} causal={causal} shape={shape}")
     qb, kb, vb = synth.normal_qkv((T, 3, D), dtype, 77 + D)
-    check_full(qb, kb, vb, dtype, causal, scale_of(D), cu=cu, tile_rows=tile_rows)
+    check_full(qb, kb, vb, dtype, causal, scale_of(D), cu=cu, shape=shape)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9, 3.0])
@@ -192,25 +197,27 @@ def test_lse_optional():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("name", ["llama", "mha_causal"])
+@pytest.mark.parametrize("name", ["llama", "mha_causal", "mha"])
 def test_tile_size_choice(name):
-    """128- and 256-row query tiles: bitwise identical O and LSE for D = 128 (same per-row
-    arithmetic over the same 64-key tiles). For D = 64 the 4-wave kernel walks 128-key tiles,
-    so the lazy maximum and the fp16 row sums are grouped differently: each result is within
-    the oracle tolerance, hence they differ by at most twice it (O) and by 5e-4 (LSE, twice the
-    2.5e-4 bound of the fp16 row sums)."""
+    """Workgroup shapes against each other. 128- and 256-row query tiles: bitwise identical O
+    and LSE for D = 128 (same per-row arithmetic over the same 64-key tiles). For D = 64 the
+    4-wave kernel walks 128-key tiles, and the key split adds two partial sums, so the lazy
+    maximum and the row sums are grouped differently: each result is within the oracle
+    tolerance, hence they differ by at most twice it (O) and by 5e-4 (LSE, twice the 2.5e-4
+    bound of the fp16 row sums)."""
     cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg, B=2 if cfg.B > 2 else cfg.B)
     outs = []
-    for rows in (128, 256):
+    for shape in SHAPE_PARAMS:
         o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D),
-                            tile_rows=rows)
+                            shape=shape)
         outs.append((o.cpu(), lse.cpu()))
     if cfg.D == 128:
-        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
-    else:
-        assert (outs[0][0].float() - outs[1][0].float()).abs().max().item() <= 2 * TOL_O[cfg.dtype]
-        assert (outs[0][1] - outs[1][1]).abs().max().item() <= 5e-4
+        assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    for a in range(len(outs)):
+        for b in range(a + 1, len(outs)):
+            assert (outs[a][0].float() - outs[b][0].float()).abs().max().item() <= 2 * TOL_O[cfg.dtype]
+            assert (outs[a][1] - outs[b][1]).abs().max().item() <= 5e-4
 
 
 def test_page_s2050_ragged_case():
