@@ -8,9 +8,11 @@ causal (Q/K/V ~ N(0,1)*0.5). Prints ONE JSON line.
 Timing: W untimed warm-up launches, then a settle phase of untimed launches
 (--settle-ms of GPU work; the chip's power management boosts and then pulls the
 shader clock back over the first tens of milliseconds of sustained load), then
-exactly K launches timed with HIP events on the launch stream. The shader
-clock and socket power are sampled (amdsmi) from a background thread over the
-timed loop and reported with the line.
+exactly K launches timed with HIP events on the launch stream. The average
+shader clock over the timed loop comes from the GPU's own counters (the
+library's attn_clock_sample, enqueued right before and after the timed
+launches); socket power is sampled with amdsmi over the settle phase and the
+timed loop.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama]
 """
@@ -99,6 +101,8 @@ class ClockSampler:
             self._thread.join()
 
     def window(self, t0: float, t1: float):
+        """amdsmi readings between two host times (its metrics refresh slowly: a
+        window of tens of milliseconds may hold stale values)."""
         if self._smi is None:
             return {"available": False, "error": self.error}
         sel = [x for x in self.samples if t0 <= x[0] <= t1]
@@ -107,8 +111,7 @@ class ClockSampler:
         per_xcd = [c for x in sel for c in x[2]] or [x[1] for x in sel if isinstance(x[1], int)]
         pw = [x[3] for x in sel if x[3] is not None]
         return {"available": True, "samples": len(sel),
-                "sclk_mhz_mean": round(sum(per_xcd) / len(per_xcd), 1),
-                "sclk_mhz_min": min(per_xcd), "sclk_mhz_max": max(per_xcd),
+                "amdsmi_sclk_mhz_mean": round(sum(per_xcd) / len(per_xcd), 1),
                 "socket_power_w_mean": round(sum(pw) / len(pw), 1) if pw else None}
 
 
@@ -186,17 +189,27 @@ def timed(step, steps: int, warmup: int, settle_ms: float, stream):
     t_w = time.perf_counter()
     step()
     torch.cuda.synchronize()
+    hs = time.perf_counter()
     st = settle(step, settle_ms, (time.perf_counter() - t_w) * 1e3)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    h0 = time.perf_counter()
+    ctr = torch.zeros(4, dtype=torch.int64, device="cuda")
+    from scaled_dot_product_08_amd import binding
+    binding.clock_sample(ctr[0:2], stream)
     t0.record(stream)
     for _ in range(steps):
         step()
     t1.record(stream)
+    binding.clock_sample(ctr[2:4], stream)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
-    return t0.elapsed_time(t1) / steps, st, (CLOCK.window(h0, h1) if CLOCK is not None else None)
+    c = ctr.cpu().tolist()
+    cycles, ticks = c[2] - c[0], c[3] - c[1]
+    clock = {"sclk_mhz": round(cycles / ticks * 100.0, 1) if ticks > 0 else None,
+             "source": "shader-clock counter of XCD 0 over the timed loop (attn_clock_sample)"}
+    if CLOCK is not None:
+        clock["settle_and_timed"] = CLOCK.window(hs, h1)
+    return t0.elapsed_time(t1) / steps, st, clock
 
 
 def time_workload(cfg, steps: int, warmup: int, samples: int = 0, settle_ms: float = 0.0,
@@ -557,7 +570,7 @@ def side(args, synth):
 def figure(r, peak=PEAK_TFLOPS):
     """Line entry of one forward workload's timing."""
     clk = r.get("clock") or {}
-    mhz = clk.get("sclk_mhz_mean")
+    mhz = clk.get("sclk_mhz")
     return {"us_per_call": round(r["ms"] * 1e3, 2), "tflops": round(r["tflops"], 1),
             "frac_of_peak": round(r["tflops"] / peak, 4),
             "per_launch_us": r.get("per_launch_us"), "settle": r.get("settle"), "clock": clk,
@@ -642,7 +655,7 @@ def main():
 
     traffic = read_traffic(args.workload)
     clk = r["clock"] or {}
-    mhz = clk.get("sclk_mhz_mean")
+    mhz = clk.get("sclk_mhz")
     line = {
         "metric": METRIC,
         "value": round(r["tflops"], 2),

@@ -279,6 +279,16 @@ int attn_version(void);
  */
 int attn_last_hip_error(void);
 
+/*
+ * Measurement support (not part of the attention path): enqueues on `stream`
+ * one wave that writes the shader-clock counter (cycles of the shader clock of
+ * the XCD it runs on) to dst[0] and the 100 MHz real-time counter to dst[1].
+ * dst is DEVICE memory for two uint64_t, 8-byte aligned (else ATTN_ERR_NULL /
+ * ATTN_ERR_ALIGN). Two samples around a timed region give its average shader
+ * clock: (dst'[0] - dst[0]) / (dst'[1] - dst[1]) * 100 MHz.
+ */
+int attn_clock_sample(uint64_t* dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

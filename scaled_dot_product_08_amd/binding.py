@@ -21,7 +21,7 @@ STATUS = {
 }
 EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version",
-           "attn_last_hip_error")
+           "attn_last_hip_error", "attn_clock_sample")
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libsdpa08.so")
 _lib = None
@@ -90,6 +90,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_version.argtypes = []
     lib.attn_last_hip_error.restype = ctypes.c_int
     lib.attn_last_hip_error.argtypes = []
+    lib.attn_clock_sample.restype = ctypes.c_int
+    lib.attn_clock_sample.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -97,6 +99,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
 
 def attn_strerror(status: int) -> str:
     return load_library().attn_strerror(int(status)).decode()
+
+
+def clock_sample(dst, stream=None) -> None:
+    """Enqueue attn_clock_sample into ``dst`` (a device int64 tensor of 2 elements)."""
+    st = load_library().attn_clock_sample(dst.data_ptr(), _stream_ptr(stream))
+    if st != 0:
+        raise AttnError(st, attn_strerror(st))
 
 
 def attn_version() -> int:

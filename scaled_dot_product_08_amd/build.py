@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsdpa08.so")
 SOURCES = ["attn_fwd_kernel.hip", "attn_fwd_fp8_kernel.hip", "attn_bwd_kernel.hip",
-           "attn_decode_kernel.hip", "attn_api.cpp"]
+           "attn_decode_kernel.hip", "attn_clock.hip", "attn_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code.

@@ -12,6 +12,7 @@
 
 #include "../../include/attn.h"
 #include "attn_bwd.h"
+#include "attn_clock.h"
 #include "attn_decode.h"
 #include "attn_fp8.h"
 #include "attn_kernel.h"
@@ -108,6 +109,13 @@ extern "C" {
 int attn_version(void) { return kVersion; }
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_clock_sample(uint64_t* dst, void* stream) {
+  if (dst == nullptr) return ATTN_ERR_NULL;
+  if (!aligned(dst, 8)) return ATTN_ERR_ALIGN;
+  clear_stale_error();
+  return launch_status(sdpa08::launch_clock_sample(dst, reinterpret_cast<hipStream_t>(stream)));
+}
 
 const char* attn_strerror(int status) {
   switch (status) {

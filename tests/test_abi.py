@@ -244,3 +244,8 @@ def test_one_hip_runtime_in_the_process(lib):
     maps = open("/proc/self/maps").read()
     hips = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hips) == 1, hips
+
+
+def test_clock_sample_argument_errors(lib):
+    assert lib.attn_clock_sample(None, None) == -1
+    assert lib.attn_clock_sample(P + 4, None) == -8
