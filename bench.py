@@ -193,20 +193,27 @@ def timed(step, steps: int, warmup: int, settle_ms: float, stream):
     st = settle(step, settle_ms, (time.perf_counter() - t_w) * 1e3)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    ctr = torch.zeros(4, dtype=torch.int64, device="cuda")
     from scaled_dot_product_08_amd import binding
-    binding.clock_sample(ctr[0:2], stream)
+    n = 2 * binding.CLOCK_SLOTS
+    ctr = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    pre = torch.cuda.Event(enable_timing=True)
+    pre.record(stream)                     # barrier: the settle launches have finished
+    binding.clock_sample(ctr[:n], stream)
     t0.record(stream)
     for _ in range(steps):
         step()
-    t1.record(stream)
-    binding.clock_sample(ctr[2:4], stream)
+    t1.record(stream)                      # barrier: the timed launches have finished
+    binding.clock_sample(ctr[n:], stream)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
     c = ctr.cpu().tolist()
-    cycles, ticks = c[2] - c[0], c[3] - c[1]
-    clock = {"sclk_mhz": round(cycles / ticks * 100.0, 1) if ticks > 0 else None,
-             "source": "shader-clock counter of XCD 0 over the timed loop (attn_clock_sample)"}
+    per = sorted(binding.clock_mhz(c[:n], c[n:]))
+    clock = {"sclk_mhz": round(per[len(per) // 2], 1) if per else None,
+             "cus": len(per),
+             "sclk_mhz_min": round(per[0], 1) if per else None,
+             "sclk_mhz_max": round(per[-1], 1) if per else None,
+             "source": "median over CUs of each CU's shader-clock counter over the timed loop "
+                       "(attn_clock_sample)"}
     if CLOCK is not None:
         clock["settle_and_timed"] = CLOCK.window(hs, h1)
     return t0.elapsed_time(t1) / steps, st, clock

@@ -281,11 +281,18 @@ int attn_last_hip_error(void);
 
 /*
  * Measurement support (not part of the attention path): enqueues on `stream`
- * one wave that writes the shader-clock counter (cycles of the shader clock of
- * the XCD it runs on) to dst[0] and the 100 MHz real-time counter to dst[1].
- * dst is DEVICE memory for two uint64_t, 8-byte aligned (else ATTN_ERR_NULL /
- * ATTN_ERR_ALIGN). Two samples around a timed region give its average shader
- * clock: (dst'[0] - dst[0]) / (dst'[1] - dst[1]) * 100 MHz.
+ * waves on every CU that record, for CU slot s (s = 128 * XCD + the CU's
+ * HW_ID bits [14:8]: shader engine, array and CU), the CU's shader-clock
+ * counter (cycles of its shader clock; the counter stops while the CU is
+ * clock-gated) in dst[2s] and the 100 MHz real-time counter in dst[2s + 1].
+ * dst is DEVICE memory for 2048 uint64_t, 8-byte aligned (else ATTN_ERR_NULL
+ * / ATTN_ERR_ALIGN); slots of absent CUs are left as they were. Counters of
+ * different CUs do not share an origin: compare two samples per slot. Over a
+ * busy region between them, (dst'[2s] - dst[2s]) / (dst'[2s+1] - dst[2s+1]) *
+ * 100 MHz is that CU's average shader clock. A kernel can start on CUs the
+ * previous kernel of the stream has released while that kernel still runs,
+ * so a sample meant to follow earlier work must be enqueued after a barrier
+ * (an event record) on the stream.
  */
 int attn_clock_sample(uint64_t* dst, void* stream);
 

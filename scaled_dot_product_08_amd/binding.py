@@ -101,11 +101,28 @@ def attn_strerror(status: int) -> str:
     return load_library().attn_strerror(int(status)).decode()
 
 
+CLOCK_SLOTS = 1024      # CU slots of attn_clock_sample (8 XCDs x 128)
+
+
 def clock_sample(dst, stream=None) -> None:
-    """Enqueue attn_clock_sample into ``dst`` (a device int64 tensor of 2 elements)."""
+    """Enqueue attn_clock_sample into ``dst`` (a device int64 tensor of 2048 elements: per CU
+    slot, its shader-clock counter and the 100 MHz real-time counter)."""
+    if dst.numel() < 2 * CLOCK_SLOTS or not dst.is_cuda or dst.element_size() != 8:
+        raise ValueError("clock_sample takes a device tensor of 2048 int64")
     st = load_library().attn_clock_sample(dst.data_ptr(), _stream_ptr(stream))
     if st != 0:
         raise AttnError(st, attn_strerror(st))
+
+
+def clock_mhz(before, after) -> list:
+    """Average shader clock (MHz) of every CU slot that both samples (host lists of 2048 ints,
+    taken from zero-filled buffers) recorded and whose counter advanced."""
+    out = []
+    for s in range(CLOCK_SLOTS):
+        t0, r0, t1, r1 = before[2 * s], before[2 * s + 1], after[2 * s], after[2 * s + 1]
+        if t0 and t1 and r1 > r0 and t1 > t0:
+            out.append((t1 - t0) / (r1 - r0) * 100.0)
+    return out
 
 
 def attn_version() -> int:

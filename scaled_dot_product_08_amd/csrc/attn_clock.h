@@ -6,7 +6,14 @@
 
 namespace sdpa08 {
 
-// Writes {shader-clock counter, 100 MHz real-time counter} to dst[0], dst[1].
+constexpr int kClockXcds = 8;           // XCDs of the device
+constexpr int kClockCusPerXcd = 128;    // slots per XCD: HW_ID's (engine, array, CU) fields
+constexpr int kClockSlots = kClockXcds * kClockCusPerXcd;
+
+// For every CU slot s (XCD x, HW_ID bits [14:8] c; s = 128 x + c):
+// dst[2s] = its shader-clock counter, dst[2s + 1] = the 100 MHz real-time
+// counter, read by a wave running on that CU. Slots of absent CUs are left
+// as they were.
 hipError_t launch_clock_sample(uint64_t* dst, hipStream_t stream);
 
 }  // namespace sdpa08

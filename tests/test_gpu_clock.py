@@ -1,5 +1,5 @@
-"""attn_clock_sample: the shader-clock and real-time counters it records advance, and their
-ratio over a sustained attention workload is a plausible shader clock."""
+"""attn_clock_sample: the per-CU shader-clock and real-time counters it records advance, and
+their ratio over a sustained attention workload is a plausible shader clock."""
 import pytest
 import torch
 
@@ -12,18 +12,22 @@ pytestmark = pytest.mark.gpu
 
 def test_clock_counters_advance_and_give_a_plausible_clock():
     st = torch.cuda.current_stream()
-    buf = torch.zeros(4, dtype=torch.int64, device="cuda")
+    n = 2 * binding.CLOCK_SLOTS
+    buf = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
     qb, kb, vb = synth.normal_qkv((2, 2048, 8, 128), "bf16", 41)
     q, k, v = (to_dev(x, "bf16") for x in (qb, kb, vb))
     binding.fwd(q, k, v, causal=True)            # warm the kernel up
-    binding.clock_sample(buf[0:2], st)
+    e0, e1 = torch.cuda.Event(), torch.cuda.Event()
+    e0.record(st)                                  # barrier before each sample
+    binding.clock_sample(buf[:n], st)
     for _ in range(50):
         binding.fwd(q, k, v, causal=True)
-    binding.clock_sample(buf[2:4], st)
+    e1.record(st)
+    binding.clock_sample(buf[n:], st)
     torch.cuda.synchronize()
     c = buf.cpu().tolist()
-    cycles, ticks = c[2] - c[0], c[3] - c[1]
-    mhz = cycles / ticks * 100.0
-    say(f"    {cycles} shader cycles over {ticks} ticks of 100 MHz: {mhz:.0f} MHz")
-    assert cycles > 0 and ticks > 0
-    assert 100.0 < mhz < 3000.0
+    per = sorted(binding.clock_mhz(c[:n], c[n:]))
+    say(f"    {len(per)} CUs: shader clock min {per[0]:.0f} median {per[len(per) // 2]:.0f} "
+        f"max {per[-1]:.0f} MHz")
+    assert len(per) >= 200, "most CUs ran a sampling wave in both samples"
+    assert 100.0 < per[len(per) // 2] < 3000.0

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import TOL_LSE, TOL_O, max_abs, say, scale_of, to_dev, to_f64
+from gpu_util import TOL_LSE, TOL_O, max_abs, record, rne_floor, say, scale_of, to_dev, to_f64
 from oracle import attention, attention_rows
 from scaled_dot_product_08_amd import binding
 
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 REL_O = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
 
 
-def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=None):
+def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=None, case=None):
     q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
     sl = None if slopes is None else torch.from_numpy(slopes).cuda()
     cud = None if cu is None else torch.from_numpy(cu).cuda()
@@ -31,7 +31,10 @@ def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=Non
     og = to_f64(o)
     eo, el = max_abs(og, oref), max_abs(lse.cpu().numpy(), lref)
     excess = float((np.abs(og - oref) - (TOL_O[dtype] + REL_O[dtype] * np.abs(oref))).max())
-    say(f"    max|dO|={eo:.3e} max|dLSE|={el:.3e} worst excess over bound={excess:.3e}")
+    floor = rne_floor(oref, dtype)
+    say(f"    max|dO|={eo:.3e} floor={floor:.3e} max|dLSE|={el:.3e} worst excess over bound={excess:.3e}")
+    if case is not None:
+        record(case, dtype, eo, el, floor=floor, n_rows=int(np.prod(oref.shape[:-1])))
     assert excess <= 0.0, (eo, excess)
     assert el <= TOL_LSE, el
 
@@ -48,7 +51,9 @@ def test_ext_padded(window, n_global, alibi, causal, D, dtype):
     say(f"ext padded S={S} D={D} {dtype} causal={causal} window={window} global={n_global} alibi={alibi}")
     qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 4000 + window + n_global)
     run_check(qb, kb, vb, dtype, causal, scale_of(D), window, n_global,
-              synth.alibi_slopes(H) if alibi else None)
+              synth.alibi_slopes(H) if alibi else None,
+              case=f"mask variant B={B} H={H} S={S} D={D} {dtype} causal={causal} window={window} "
+                   f"global={n_global} alibi={alibi}")
 
 
 @pytest.mark.parametrize("window,n_global,alibi", [(64, 0, False), (50, 10, True), (0, 0, True)])
@@ -60,7 +65,9 @@ def test_ext_packed(window, n_global, alibi, causal):
     say(f"ext packed causal={causal} window={window} global={n_global} alibi={alibi}")
     qb, kb, vb = synth.normal_qkv((T, H, D), "bf16", 4100)
     run_check(qb, kb, vb, "bf16", causal, scale_of(D), window, n_global,
-              synth.alibi_slopes(H) if alibi else None, cu=cu)
+              synth.alibi_slopes(H) if alibi else None, cu=cu,
+              case=f"mask variant packed H={H} D={D} bf16 causal={causal} window={window} "
+                   f"global={n_global} alibi={alibi}")
 
 
 def test_ext_zero_slopes_match_plain():
@@ -86,21 +93,29 @@ def test_window_one_returns_v_bitwise():
 
 
 def test_long_window_global_sampled():
-    """The pages' long-context scheme: window 4096 plus 64 global query rows, B1 H32 S65536 D128."""
+    """The pages' long-context scheme: window 4096 plus 64 global query rows, B1 H32 S65536 D128;
+    96 sampled rows (global, window-edge and interior ones) of every head."""
     S, H, D, W, G = 65536, 32, 128, 4096, 64
     say(f"window workload S={S} H={H} D={D} window={W} global={G}")
     qb, kb, vb = synth.normal_qkv((1, S, H, D), "bf16", 4400)
     q, k, v = (to_dev(x, "bf16") for x in (qb, kb, vb))
     o, lse = binding.fwd(q, k, v, causal=True, window=W, n_global=G)
     torch.cuda.synchronize()
-    rows = synth.sampled_rows(S, 48, 4401, must=(0, 1, 63, 64, 65, 4095, 4096, 4097))
-    heads = [0, 17, 31]
-    f = [synth.bits_to_f64(x[0][:, heads], "bf16") for x in (qb, kb, vb)]
-    oref, lref = attention_rows(*f, rows, causal=True, scale=scale_of(D), window=W, n_global=G)
+    rows = synth.sampled_rows(S, 96, 4401, must=(0, 1, 63, 64, 65, 4095, 4096, 4097, S - 1))
     o, lse = o.cpu(), lse.cpu()
-    og = o[0][rows][:, heads].float().numpy().astype(np.float64)
-    eo = max_abs(og, oref)
-    el = max_abs(lse[0][heads][:, rows].numpy(), lref)
-    excess = float((np.abs(og - oref) - (TOL_O["bf16"] + REL_O["bf16"] * np.abs(oref))).max())
-    say(f"    sampled max|dO|={eo:.3e} max|dLSE|={el:.3e} excess={excess:.3e}")
+    eo = el = floor = 0.0
+    excess = -float("inf")
+    for h0 in range(0, H, 8):
+        heads = list(range(h0, h0 + 8))
+        f = [synth.bits_to_f64(x[0][:, heads], "bf16") for x in (qb, kb, vb)]
+        oref, lref = attention_rows(*f, rows, causal=True, scale=scale_of(D), window=W, n_global=G)
+        og = o[0][rows][:, heads].float().numpy().astype(np.float64)
+        eo = max(eo, max_abs(og, oref))
+        el = max(el, max_abs(lse[0][heads][:, rows].numpy(), lref))
+        excess = max(excess, float((np.abs(og - oref)
+                                    - (TOL_O["bf16"] + REL_O["bf16"] * np.abs(oref))).max()))
+        floor = max(floor, rne_floor(oref, "bf16"))
+    say(f"    sampled max|dO|={eo:.3e} floor={floor:.3e} max|dLSE|={el:.3e} excess={excess:.3e}")
+    record(f"mask variant B=1 H={H} S={S} D={D} bf16 causal window={W} global={G} "
+           f"(96 sampled rows of every head)", "bf16", eo, el, floor=floor, n_rows=len(rows) * H)
     assert excess <= 0.0 and el <= TOL_LSE
