@@ -6,9 +6,11 @@ Default workload: the LLaMA-2-7B-shaped layer, B=4 H=32 S=4096 D=128 bf16
 causal (Q/K/V ~ N(0,1)*0.5). Prints ONE JSON line.
 
 Timing: W untimed warm-up launches, then a settle phase of untimed launches
-(--settle-ms of GPU work; the chip's power management boosts and then pulls the
-shader clock back over the first tens of milliseconds of sustained load), then
-exactly K launches timed with HIP events on the launch stream. The average
+(--settle-ms of GPU work; the chip's power management runs the shader clock
+low for the first tens of milliseconds after the GPU has been idle), then
+exactly K launches timed with HIP events on the launch stream. The host does
+not wait between the settle launches and the timed ones, so the GPU runs from
+one into the other without idling. The average
 shader clock over the timed loop comes from the GPU's own counters (the
 library's attn_clock_sample, enqueued right before and after the timed
 launches); socket power is sampled with amdsmi over the settle phase and the
@@ -164,19 +166,24 @@ def make_device_inputs(cfg):
 
 
 def settle(step, settle_ms: float, per_launch_ms: float):
-    """Untimed launches until about ``settle_ms`` of GPU work has run."""
+    """Untimed launches until about ``settle_ms`` of GPU work has been enqueued. The host
+    waits for every chunk but the last, so the GPU goes from the settle launches straight
+    into whatever is enqueued next, with no idle gap: after even a short idle period the
+    power management brings the shader clock back up over the next tens of milliseconds."""
     import torch
     if settle_ms <= 0:
-        return {"launches": 0, "seconds": 0.0}
+        return {"launches": 0, "ms_of_gpu_work": 0.0, "host_wait_before_timing": True}
     n = 0
-    t0 = time.perf_counter()
     chunk = max(1, int(20.0 / max(per_launch_ms, 1e-3)))      # ~20 ms per chunk
-    while (time.perf_counter() - t0) * 1e3 < settle_ms:
-        for _ in range(chunk):
+    target = max(1, int(settle_ms / max(per_launch_ms, 1e-3)))
+    while n < target:
+        if n:
+            torch.cuda.synchronize()
+        for _ in range(min(chunk, target - n)):
             step()
-        n += chunk
-        torch.cuda.synchronize()
-    return {"launches": n, "seconds": round(time.perf_counter() - t0, 3)}
+        n += min(chunk, target - n)
+    return {"launches": n, "ms_of_gpu_work": round(n * per_launch_ms, 1),
+            "host_wait_before_timing": False}
 
 
 def timed(step, steps: int, warmup: int, settle_ms: float, stream):
@@ -190,13 +197,17 @@ def timed(step, steps: int, warmup: int, settle_ms: float, stream):
     step()
     torch.cuda.synchronize()
     hs = time.perf_counter()
-    st = settle(step, settle_ms, (time.perf_counter() - t_w) * 1e3)
+    per_launch_ms = (hs - t_w) * 1e3
+    # Everything the timed region needs is allocated before the settle launches,
+    # so nothing between them and the timed loop can wait for the device.
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    pre = torch.cuda.Event(enable_timing=True)
     from scaled_dot_product_08_amd import binding
     n = 2 * binding.CLOCK_SLOTS
     ctr = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
-    pre = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st = settle(step, settle_ms, per_launch_ms)
     pre.record(stream)                     # barrier: the settle launches have finished
     binding.clock_sample(ctr[:n], stream)
     t0.record(stream)
@@ -670,7 +681,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle": {**r["settle"], "note": "untimed launches between warm-up and the timed loop"},
+        "settle": {**r["settle"], "note": "untimed launches between warm-up and the timed loop, enqueued back to back with it"},
         "ms_per_step": round(r["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
