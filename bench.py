@@ -37,9 +37,11 @@ PEAK_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA: 256 CU x 2.4 GHz x 
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E peak bandwidth
 PEAK_TFLOPS_FP8 = 5033.2      # MI355X dense fp8 MFMA: twice the fp16/bf16 rate
 KERNEL_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_fwd_kernel.hip",
-                  "scaled_dot_product_08_amd/csrc/attn_kernel.h"]
+                  "scaled_dot_product_08_amd/csrc/attn_kernel.h",
+                  "scaled_dot_product_08_amd/csrc/gfx950_util.h"]
 DECODE_SOURCES = ["scaled_dot_product_08_amd/csrc/attn_decode_kernel.hip",
-                  "scaled_dot_product_08_amd/csrc/attn_decode.h"]
+                  "scaled_dot_product_08_amd/csrc/attn_decode.h",
+                  "scaled_dot_product_08_amd/csrc/gfx950_util.h"]
 
 
 # The pages' own attention-forward figures, for context only (other hardware):

@@ -62,10 +62,15 @@ def rne_floor(oref: np.ndarray, dtype: str) -> float:
 
 
 def record(case: str, dtype: str, eo: float, el: float, oref=None, n_rows: int | None = None,
-           floor: float | None = None, tol_o: float | None = None):
-    """Remember one case's largest errors (and the rounding floor of its exact output)."""
+           floor: float | None = None, tol_o: float | None = None, excess: float | None = None):
+    """Remember one case's largest errors (and the rounding floor of its exact output).
+    ``excess``: for cases held to a per-element bound, the largest |dO| minus that bound
+    (at most 0 when the case passes)."""
     if floor is None and oref is not None:
         floor = rne_floor(oref, dtype)
-    MARGINS.append({"case": case, "dtype": dtype, "max_abs_dO": eo, "max_abs_dLSE": el,
-                    "tol_O": TOL_O[dtype] if tol_o is None else tol_o, "tol_LSE": TOL_LSE,
-                    "rne_floor_O": floor, "rows_checked": n_rows})
+    rec = {"case": case, "dtype": dtype, "max_abs_dO": eo, "max_abs_dLSE": el,
+           "tol_O": TOL_O[dtype] if tol_o is None else tol_o, "tol_LSE": TOL_LSE,
+           "rne_floor_O": floor, "rows_checked": n_rows}
+    if excess is not None:
+        rec["worst_excess_over_bound"] = excess
+    MARGINS.append(rec)

@@ -34,7 +34,7 @@ def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=Non
     floor = rne_floor(oref, dtype)
     say(f"    max|dO|={eo:.3e} floor={floor:.3e} max|dLSE|={el:.3e} worst excess over bound={excess:.3e}")
     if case is not None:
-        record(case, dtype, eo, el, floor=floor, n_rows=int(np.prod(oref.shape[:-1])))
+        record(case, dtype, eo, el, floor=floor, n_rows=int(np.prod(oref.shape[:-1])), excess=excess)
     assert excess <= 0.0, (eo, excess)
     assert el <= TOL_LSE, el
 
@@ -117,5 +117,6 @@ def test_long_window_global_sampled():
         floor = max(floor, rne_floor(oref, "bf16"))
     say(f"    sampled max|dO|={eo:.3e} floor={floor:.3e} max|dLSE|={el:.3e} excess={excess:.3e}")
     record(f"mask variant B=1 H={H} S={S} D={D} bf16 causal window={W} global={G} "
-           f"(96 sampled rows of every head)", "bf16", eo, el, floor=floor, n_rows=len(rows) * H)
+           f"(96 sampled rows of every head)", "bf16", eo, el, floor=floor, n_rows=len(rows) * H,
+           excess=excess)
     assert excess <= 0.0 and el <= TOL_LSE
