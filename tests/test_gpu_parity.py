@@ -64,6 +64,17 @@ def test_config_mha_full(name):
                case=name + " " + cfg.describe() + " (every output)")
 
 
+@pytest.mark.parametrize("wg", [(128, 2), (256, 1)], ids=["bm128ks2", "bm256"])
+@pytest.mark.parametrize("name", ["mha", "mha_causal"])
+def test_config_mha_full_other_shapes(name, wg):
+    """The B=4 H=12 S=2048 D=64 workloads with the workgroup shapes the size heuristic does
+    not pick for them (the key split and 256-row tiles), every output against the oracle."""
+    cfg = synth.CONFIGS[name]
+    say(name, cfg.describe(), "shape", wg)
+    inp = synth.make_inputs(cfg)
+    check_full(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D), shape=wg)
+
+
 def _sampled_padded(cfg, rows_per_head, heads_stride=1, seed_off=2, case=None):
     inp = synth.make_inputs(cfg)
     scale = scale_of(cfg.D)
