@@ -621,7 +621,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the (batch, head) split needs no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
 

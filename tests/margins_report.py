@@ -48,9 +48,9 @@ def render(d: dict, n_tests: int | None, source: str | None) -> str:
            "Command (on one MI355X, from the repository root, after building):",
            "",
            "```",
-           "ATTN_PARITY_REPORT=gpurun_out/parity_margins.json python -u -m pytest tests -m gpu -x -q \\",
+           "ATTN_PARITY_REPORT=/tmp/parity_margins.json python -u -m pytest tests -m gpu -x -q \\",
            "    --timeout 300 --timeout-method thread",
-           "python tests/margins_report.py gpurun_out/parity_margins.json profiles/parity_margins.md",
+           "python tests/margins_report.py /tmp/parity_margins.json profiles/parity_margins.md",
            "```",
            "",
            f"Result: {status}" + (f"; forward kernel source `{source}`." if source else "."),
