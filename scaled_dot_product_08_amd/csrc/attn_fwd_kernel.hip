@@ -47,6 +47,11 @@ constexpr int HEAD_GROUP = 4; // heads whose query tiles are interleaved on one 
 constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 constexpr float OPT_LIMIT = 32768.0f;   // largest probability the optimistic pass accepts (fp16-safe)
 
+// Softmax schemes of one key tile (see compute_tile).
+constexpr int TILE_OPT = 0, TILE_MAX = 1, TILE_FAST = 2;
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+template <int M> struct ModeTag { static constexpr int value = M; };
+
 // acc + lo(p) + hi(p) for a pair of fp16 values (one v_dot2).
 __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -85,6 +90,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   // and does not wait for those loads before every read.
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
+  __shared__ int redo_flag;     // some wave saw a probability above OPT_LIMIT
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,20 +246,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
   float m_run = -INFINITY;     // running max of the log2-scaled logits
   float l_run = 0.0f;          // this lane's half of the running exp-sum
+  uint64_t bad = 0;            // TILE_FAST: lanes whose tile sum failed the bound
+  // The plain instances (no mask variant, no key split) walk their tiles after
+  // the first with TILE_FAST: every row sees key 0 of its first tile, so the
+  // first tile's row maximum is finite and serves as the reference for the rest.
+  constexpr bool FAST_LOOP = !EXT && KS == 1;
 
-  auto compute_tile = [&](int j, const uint8_t* stage) {
+  // One key tile. MASKED (compile time): the tile may hold keys some row of the
+  // workgroup must not see (diagonal, sequence end, mask variants); without it
+  // the mask code is left out. MODE (compile time) picks the softmax scheme:
+  //   TILE_OPT:  optimistic exponentials, checked on the spot (redone against a
+  //              refreshed maximum when the check fails);
+  //   TILE_MAX:  the tile's row maximum first, then the exponentials;
+  //   TILE_FAST: optimistic exponentials against the running maximum with no
+  //              branch between them and P V; the check only raises `bad`,
+  //              which the workgroup acts on after its last tile.
+  auto compute_tile = [&](auto masked_c, auto mode_c, int j, const uint8_t* stage) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    constexpr int MODE = decltype(mode_c)::value;
     const uint8_t* ks = stage + kgrp * TILEB;
     const uint8_t* vs = stage + GTILEB + kgrp * TILEB;
     const int key0 = j * GBN + kgrp * BN;
     // A wave none of whose rows sees a key of this tile has nothing to do.
-    if constexpr (EXT) {
-      if (!w_any_glob) {
+    if constexpr (MASKED) {
+      if constexpr (EXT) {
+        if (!w_any_glob) {
+          if (CAUSAL && key0 > wq0 + 31) return;
+          if (win > 0 && key0 + BN - 1 <= wq0 - win) return;
+          if (win > 0 && !CAUSAL && key0 >= wq0 + 31 + win) return;
+        }
+      } else {
         if (CAUSAL && key0 > wq0 + 31) return;
-        if (win > 0 && key0 + BN - 1 <= wq0 - win) return;
-        if (win > 0 && !CAUSAL && key0 >= wq0 + 31 + win) return;
       }
-    } else {
-      if (CAUSAL && key0 > wq0 + 31) return;
     }
 
     // S^T = K Q^T for two 32-key blocks. The two accumulation chains
@@ -291,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 
     // Mask keys past the sequence end and, under causality, keys after the
     // query (only tiles that reach those positions pay for it).
-    bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
+    bool need_mask = MASKED && ((key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0));
     if constexpr (EXT) {
       // every row of the wave sees every key of the tile, or not
       bool all_vis = key0 + BN <= L;
@@ -382,8 +406,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     // maximum taken, refreshed and the exponentials redone. Softmax does not
     // depend on which constant is subtracted, so this changes rounding only.
     float tile_l = 0.0f;
-    bool redo = true;
-    if (j != j_lo) {
+    bool redo = MODE != TILE_FAST;
+    if constexpr (MODE == TILE_FAST) {
+      tile_l = exps(m_run);
+      bad |= __builtin_amdgcn_ballot_w64(!(tile_l <= OPT_LIMIT));
+    } else if (MODE == TILE_OPT && j != j_lo) {
       tile_l = exps(m_run);
       redo = __builtin_amdgcn_ballot_w64(!(tile_l <= OPT_LIMIT)) != 0;
     }
@@ -437,20 +464,82 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   };
 
   // ---- main loop: two-stage LDS ring, unrolled by two ----------------------
+  constexpr BoolTag<true> masked_t{};
+  constexpr BoolTag<false> plain_t{};
+  if (tid == 0) redo_flag = 0;
   issue_tile(j_lo, 0);
   wait_vmem_all();
   __syncthreads();
+  if constexpr (!FAST_LOOP) {
 #pragma unroll 1
-  for (int j = j_lo; j < n_kv; j += 2) {
-    if (j + 1 < n_kv) issue_tile(j + 1, 1);
-    compute_tile(j, smem0);
+    for (int j = j_lo; j < n_kv; j += 2) {
+      if (j + 1 < n_kv) issue_tile(j + 1, 1);
+      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j, smem0);
+      wait_vmem_all();
+      __syncthreads();
+      if (j + 1 >= n_kv) break;
+      if (j + 2 < n_kv) issue_tile(j + 2, 0);
+      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j + 1, smem1);
+      wait_vmem_all();
+      __syncthreads();
+    }
+  } else {
+    // Tiles before j_plain hold no key that any row of the workgroup must not
+    // see: they run without the mask code, in a loop of their own (a branch
+    // between the two kinds inside one loop makes the compiler copy the
+    // accumulators at every join). Their count after the first tile is kept
+    // even so that the masked loop always starts on stage 1.
+    int j_plain = min(n_kv, L / GBN);
+    if (CAUSAL) j_plain = min(j_plain, (q0 + 1) / GBN);
+    j_plain = j_lo + 1 + (max(0, j_plain - (j_lo + 1)) & ~1);
+    // First tile: row maxima, the reference of the optimistic tiles after it.
+    if (j_lo + 1 < n_kv) issue_tile(j_lo + 1, 1);
+    compute_tile(masked_t, ModeTag<TILE_MAX>{}, j_lo, smem0);
     wait_vmem_all();
     __syncthreads();
-    if (j + 1 >= n_kv) break;
-    if (j + 2 < n_kv) issue_tile(j + 2, 0);
-    compute_tile(j + 1, smem1);
-    wait_vmem_all();
+#pragma unroll 1
+    for (int j = j_lo + 1; j < j_plain; j += 2) {
+      issue_tile(j + 1, 0);
+      compute_tile(plain_t, ModeTag<TILE_FAST>{}, j, smem1);
+      wait_vmem_all();
+      __syncthreads();
+      if (j + 2 < n_kv) issue_tile(j + 2, 1);
+      compute_tile(plain_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+      wait_vmem_all();
+      __syncthreads();
+    }
+#pragma unroll 1
+    for (int j = j_plain; j < n_kv; j += 2) {
+      if (j + 1 < n_kv) issue_tile(j + 1, 0);
+      compute_tile(masked_t, ModeTag<TILE_FAST>{}, j, smem1);
+      wait_vmem_all();
+      __syncthreads();
+      if (j + 1 >= n_kv) break;
+      if (j + 2 < n_kv) issue_tile(j + 2, 1);
+      compute_tile(masked_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+      wait_vmem_all();
+      __syncthreads();
+    }
+    // Some tile of some wave exceeded the bound (its maximum grew by more than
+    // log2(OPT_LIMIT) over the first tile's): the whole workgroup walks its keys
+    // again from scratch, every tile's row maximum first. Every load has landed
+    // and every wave is past its last barrier, so the ring is free.
+    if (bad != 0 && lane == 0) redo_flag = 1;
     __syncthreads();
+    if (redo_flag != 0) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.0f;
+#pragma unroll 1
+      for (int j = j_lo; j < n_kv; ++j) {
+        issue_tile(j, 0);
+        wait_vmem_all();
+        __syncthreads();
+        compute_tile(masked_t, ModeTag<TILE_MAX>{}, j, smem0);
+        __syncthreads();
+      }
+    }
   }
 
   if constexpr (KS == 2) {
