@@ -48,7 +48,7 @@ constexpr float LAZY_RESCALE_LOG2 = 8.0f;
 constexpr float OPT_LIMIT = 32768.0f;   // largest probability the optimistic pass accepts (fp16-safe)
 
 // Softmax schemes of one key tile (see compute_tile).
-constexpr int TILE_OPT = 0, TILE_MAX = 1, TILE_FAST = 2;
+constexpr int TILE_OPT = 0, TILE_MAX = 1, TILE_FAST = 2, TILE_FIRST = 3;
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <int M> struct ModeTag { static constexpr int value = M; };
 
@@ -260,7 +260,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   //   TILE_MAX:  the tile's row maximum first, then the exponentials;
   //   TILE_FAST: optimistic exponentials against the running maximum with no
   //              branch between them and P V; the check only raises `bad`,
-  //              which the workgroup acts on after its last tile.
+  //              which the workgroup acts on after its last tile;
+  //   TILE_FIRST: a wave's first tile when each of its rows sees a key of it:
+  //              the row maximum becomes the running maximum (the accumulator
+  //              and the sum are still zero), again with no branch.
   auto compute_tile = [&](auto masked_c, auto mode_c, int j, const uint8_t* stage) {
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int MODE = decltype(mode_c)::value;
@@ -406,8 +409,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     // maximum taken, refreshed and the exponentials redone. Softmax does not
     // depend on which constant is subtracted, so this changes rounding only.
     float tile_l = 0.0f;
-    bool redo = MODE != TILE_FAST;
-    if constexpr (MODE == TILE_FAST) {
+    bool redo = MODE == TILE_OPT || MODE == TILE_MAX;
+    if constexpr (MODE == TILE_FIRST) {
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      m_run = half_max(mx) * c_log2;
+      tile_l = exps(m_run);
+    } else if constexpr (MODE == TILE_FAST) {
       tile_l = exps(m_run);
       bad |= __builtin_amdgcn_ballot_w64(!(tile_l <= OPT_LIMIT));
     } else if (MODE == TILE_OPT && j != j_lo) {
@@ -494,7 +508,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     j_plain = j_lo + 1 + (max(0, j_plain - (j_lo + 1)) & ~1);
     // First tile: row maxima, the reference of the optimistic tiles after it.
     if (j_lo + 1 < n_kv) issue_tile(j_lo + 1, 1);
-    compute_tile(masked_t, ModeTag<TILE_MAX>{}, j_lo, smem0);
+    compute_tile(masked_t, ModeTag<TILE_FIRST>{}, j_lo, smem0);
     wait_vmem_all();
     __syncthreads();
 #pragma unroll 1
