@@ -36,6 +36,10 @@ namespace {
 constexpr int NW = 4;           // waves per workgroup
 constexpr int BM = kBwdTileRows; // rows owned by a workgroup (32 per wave)
 constexpr int BN = 64;          // rows per streamed LDS tile
+static_assert(BM == 2 * BN, "a workgroup's rows span two streamed tiles");
+// Compile-time flag of a tile body: the tile may hold positions some row must
+// not see (a diagonal or a sequence end); without it the mask code is left out.
+template <bool B> struct MaskTag { static constexpr bool value = B; };
 constexpr int HEAD_GROUP = 4;   // heads whose tiles are interleaved on one XCD
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -228,10 +232,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
 
-  auto compute_tile = [&](int j, const uint8_t* ks) {
+  auto compute_tile = [&](auto masked_c, int j, const uint8_t* ks) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const uint8_t* vs = ks + TILEB;
     const int key0 = j * BN;
-    if (CAUSAL && key0 > wq0 + 31) return;     // no row of this wave sees the tile
+    if (MASKED && CAUSAL && key0 > wq0 + 31) return;     // no row of this wave sees the tile
 
     // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks each.
     f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
     }
 
     // P^T = exp2(s * c - lse2), dS^T = P^T (dP^T - delta), packed to 16 bit.
-    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
+    const bool need_mask = MASKED && ((key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0));
     uint32_t pk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -282,18 +287,38 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // Key tiles before j_plain hold no key that any row of the workgroup must not
+  // see: they run without the mask code, in a loop of their own (the mask's
+  // lane-dependent condition would otherwise cost every tile its exec-mask
+  // handling). Their count is kept even so the masked loop starts on stage 0.
+  int j_plain = min(n_kv, L / BN);
+  if (CAUSAL) j_plain = min(j_plain, (q0 + 1) / BN);
+  j_plain &= ~1;
+  constexpr MaskTag<true> masked_t{};
+  constexpr MaskTag<false> plain_t{};
   issue_tile(0, 0);
   wait_vmem_all();
   __syncthreads();
 #pragma unroll 1
-  for (int j = 0; j < n_kv; j += 2) {
+  for (int j = 0; j < j_plain; j += 2) {
+    issue_tile(j + 1, 1);
+    compute_tile(plain_t, j, smem0);
+    wait_vmem_all();
+    __syncthreads();
+    if (j + 2 < n_kv) issue_tile(j + 2, 0);
+    compute_tile(plain_t, j + 1, smem1);
+    wait_vmem_all();
+    __syncthreads();
+  }
+#pragma unroll 1
+  for (int j = j_plain; j < n_kv; j += 2) {
     if (j + 1 < n_kv) issue_tile(j + 1, 1);
-    compute_tile(j, smem0);
+    compute_tile(masked_t, j, smem0);
     wait_vmem_all();
     __syncthreads();
     if (j + 1 >= n_kv) break;
     if (j + 2 < n_kv) issue_tile(j + 2, 0);
-    compute_tile(j + 1, smem1);
+    compute_tile(masked_t, j + 1, smem1);
     wait_vmem_all();
     __syncthreads();
   }
@@ -393,15 +418,16 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) v
     acc_v[d] = f32x16{};
   }
 
-  auto compute_tile = [&](int j, const uint8_t* qs) {
+  auto compute_tile = [&](auto masked_c, int j, const uint8_t* qs) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const uint8_t* dos = qs + TILEB;
     const float* lse_t = reinterpret_cast<const float*>(qs + 2 * TILEB);
     const float* del_t = reinterpret_cast<const float*>(qs + 2 * TILEB + 1024);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int qb0 = j * BN + kb * 32;      // first query row of this block
-      if (qb0 >= L) continue;
-      if (CAUSAL && qb0 + 31 < wk0) continue;  // every row precedes every key of the wave
+      if (MASKED && qb0 >= L) continue;
+      if (MASKED && CAUSAL && qb0 + 31 < wk0) continue;  // every row precedes every key of the wave
 
       // S = Q K^T and dP = dO V^T: lane = key, registers = query rows.
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -415,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) v
         }
       }
 
-      const bool need_mask = (qb0 + 32 > L) || (CAUSAL && qb0 < wk0 + 31);
+      const bool need_mask = MASKED && ((qb0 + 32 > L) || (CAUSAL && qb0 < wk0 + 31));
       uint32_t pp[8], pd[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -464,22 +490,37 @@ __global__ __launch_bounds__(NW * 64, (D == 128 && MODE == DKDV_BOTH) ? 1 : 2) v
     }
   };
 
+  // Query tiles in [j_pl, j_ph) see every key of the workgroup from their
+  // first row on and lie inside the sequence: they run without the mask code in
+  // a loop of their own. Before them come the diagonal tiles (two: the
+  // workgroup's 128 keys span two 64-row tiles), after them the tail; the
+  // plain count is kept even so each loop starts on stage 0.
+  int j_pl = CAUSAL ? min(n_q, j_lo + 2) : j_lo;
+  int j_ph = max(j_pl, min(n_q, L / BN));
+  j_ph = j_pl + ((j_ph - j_pl) & ~1);
+  constexpr MaskTag<true> masked_t{};
+  constexpr MaskTag<false> plain_t{};
+  auto walk = [&](auto masked_c, int ja, int jb) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int j = ja; j < jb; j += 2) {
+      if (j + 1 < n_q) issue_tile(j + 1, 1);
+      compute_tile(masked_c, j, smem0);
+      wait_vmem_all();
+      __syncthreads();
+      if (j + 1 >= jb) break;
+      if (j + 2 < n_q) issue_tile(j + 2, 0);
+      compute_tile(masked_c, j + 1, smem1);
+      wait_vmem_all();
+      __syncthreads();
+    }
+  };
   if (j_lo < n_q) {
     issue_tile(j_lo, 0);
     wait_vmem_all();
     __syncthreads();
-#pragma unroll 1
-    for (int j = j_lo; j < n_q; j += 2) {
-      if (j + 1 < n_q) issue_tile(j + 1, 1);
-      compute_tile(j, smem0);
-      wait_vmem_all();
-      __syncthreads();
-      if (j + 1 >= n_q) break;
-      if (j + 2 < n_q) issue_tile(j + 2, 0);
-      compute_tile(j + 1, smem1);
-      wait_vmem_all();
-      __syncthreads();
-    }
+    walk(masked_t, j_lo, j_pl);
+    walk(plain_t, j_pl, j_ph);
+    walk(masked_t, j_ph, n_q);
   }
 
   const __amdgpu_buffer_rsrc_t dk_rsrc = make_rsrc(p.dk + kbase, k_rows * tok_bytes);
