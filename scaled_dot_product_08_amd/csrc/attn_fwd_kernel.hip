@@ -3,7 +3,9 @@
 // One workgroup of NW waves (NW = 4 or 8) owns a tile of BM = 32*NW query rows
 // of one (sequence, head); wave w owns rows 32w..32w+31 of the tile. The kernel
 // streams the visible keys in tiles of BN rows (64; 128 for D = 64, 4 waves) through a
-// two-stage LDS ring and, per tile, runs the fused chain of mlqm.cn/news/343191 §3.1
+// two-stage LDS ring (three stages for the 8-wave D = 128 plain instances, whose two
+// wave groups run the tile chain half a tile apart) and, per tile, runs the fused
+// chain of mlqm.cn/news/343191 §3.1
 // (Q K^T -> scale -> mask -> softmax -> P V) with the online softmax of
 // jianying88.com/news/49672 §3: a running row maximum m and exponential sum l
 // per query row, so no score ever leaves registers.
@@ -52,6 +54,39 @@ constexpr int TILE_OPT = 0, TILE_MAX = 1, TILE_FAST = 2, TILE_FIRST = 3;
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <int M> struct ModeTag { static constexpr int value = M; };
 
+// MFMA order of one matrix phase of the ping-pong schedule (see the kernel):
+// MODE PP_FULL runs P V of the previous tile and Q K^T of this one, the first AH
+// MFMAs P V (their V operands are read before the barrier that opens the
+// phase), then Q K^T and P V alternating, then the rest of Q K^T (so that no
+// accumulation chain waits on its own previous result); PP_QK and PP_PV run one
+// product alone. kind(n): 0 = P V, 1 = Q K^T; idx(n): which MFMA of that product.
+constexpr int PP_FULL = 0, PP_QK = 1, PP_PV = 2;
+template <int MODE, int AH, int NPV, int NQK> struct PPOrder {
+  static constexpr int total = MODE == PP_FULL ? NPV + NQK : (MODE == PP_QK ? NQK : NPV);
+  static constexpr int kind(int n) {
+    if (MODE != PP_FULL) return MODE == PP_QK ? 1 : 0;
+    if (n < AH) return 0;
+    const int r = n - AH, pl = NPV - AH;
+    return (r < 2 * pl && (r & 1)) ? 0 : 1;
+  }
+  static constexpr int idx(int n) {
+    if (MODE != PP_FULL || n < AH) return n;
+    const int r = n - AH, pl = NPV - AH;
+    if (r < 2 * pl) return (r & 1) ? AH + (r >> 1) : (r >> 1);
+    return pl + (r - 2 * pl);
+  }
+  static constexpr int reads(int n) { return kind(n) == 0 ? 2 : 1; }   // LDS reads of operand A
+  static constexpr int reads_before(int n) { return n <= 0 ? 0 : reads(n - 1) + reads_before(n - 1); }
+};
+// Scheduling groups of a matrix phase: before MFMA n, the reads of MFMA n + AH.
+template <class O, int AH, int N> __device__ __forceinline__ void pp_groups() {
+  if constexpr (N < O::total) {
+    if constexpr (N + AH < O::total) __builtin_amdgcn_sched_group_barrier(0x100, O::reads(N + AH), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    pp_groups<O, AH, N + 1>();
+  }
+}
+
 // acc + lo(p) + hi(p) for a pair of fp16 values (one v_dot2).
 __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -91,6 +126,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
   __shared__ int redo_flag;     // some wave saw a probability above OPT_LIMIT
+  // The 8-wave D = 128 plain instances run the ping-pong schedule (below) on a
+  // three-stage ring.
+  constexpr bool PINGPONG = !EXT && KS == 1 && NW == 8 && D == 128;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,13 +260,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     }
   }
 
-  // Issue the direct loads of key tile j into stage `st`.
-  auto issue_tile = [&](int j, int st) {
+  // Issue the direct loads of key tile j into `stage` (K tile, then V tile).
+  auto issue_to = [&](int j, uint8_t* stage) {
     const int key0 = j * GBN;
     const uint32_t rows = (uint32_t)min(L - key0, GBN);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
-    uint8_t* kdst = (st ? smem1 : smem0) + wave * LDW * 1024;
+    uint8_t* kdst = stage + wave * LDW * 1024;
     uint8_t* vdst = kdst + GTILEB;
 #pragma unroll
     for (int u = 0; u < LDW; ++u) {
@@ -239,6 +277,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
     }
   };
+  auto issue_tile = [&](int j, int st) { issue_to(j, st ? smem1 : smem0); };
 
   // ---- running statistics and accumulator --------------------------------
   f32x16 acc[DB];
@@ -477,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     }
   };
 
-  // ---- main loop: two-stage LDS ring, unrolled by two ----------------------
+  // ---- main loop ---------------------------------------------------------------
   constexpr BoolTag<true> masked_t{};
   constexpr BoolTag<false> plain_t{};
   if (tid == 0) redo_flag = 0;
@@ -498,41 +537,261 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       __syncthreads();
     }
   } else {
-    // Tiles before j_plain hold no key that any row of the workgroup must not
-    // see: they run without the mask code, in a loop of their own (a branch
-    // between the two kinds inside one loop makes the compiler copy the
-    // accumulators at every join). Their count after the first tile is kept
-    // even so that the masked loop always starts on stage 1.
-    int j_plain = min(n_kv, L / GBN);
-    if (CAUSAL) j_plain = min(j_plain, (q0 + 1) / GBN);
-    j_plain = j_lo + 1 + (max(0, j_plain - (j_lo + 1)) & ~1);
-    // First tile: row maxima, the reference of the optimistic tiles after it.
-    if (j_lo + 1 < n_kv) issue_tile(j_lo + 1, 1);
-    compute_tile(masked_t, ModeTag<TILE_FIRST>{}, j_lo, smem0);
-    wait_vmem_all();
-    __syncthreads();
+    if constexpr (PINGPONG) {
+      // Ping-pong schedule. Waves w and w + 4 share a SIMD. Each wave alternates
+      // a matrix phase M(t) (P V of tile t-1, then Q K^T of tile t) and a vector
+      // phase S(t) (the softmax of tile t), with a workgroup barrier after every
+      // phase; waves 4-7 run one phase behind waves 0-3, so on every SIMD one
+      // wave's MFMAs overlap the other's exponentials instead of both waves
+      // entering the same phase together. A single wave keeps the matrix core
+      // fed only if its LDS operands are read well ahead: each MFMA's operand is
+      // read PP_AH MFMAs before it, and the first PP_AH (V operands) before the
+      // barrier that opens the phase.
+      //   Phase p:   0     1     2     3     ...  2t    2t+1  ...  2n    2n+1
+      //   waves 0-3: M(0)  S(0)  M(1)  S(1)       M(t)  S(t)       M(n)
+      //   waves 4-7: -     M(0)  S(0)  M(1)       S(t-1) M(t)      S(n-1) M(n)
+      // Tile t sits in stage t % 3. Its loads go out at the start of phase 2t-2
+      // (when the stage's previous tile, t-3, was last read: its V in phase
+      // 2t-3) and are waited for at the end of phase 2t-1, so the Q K^T of
+      // phase 2t and the V reads issued during phase 2t+1 find them in LDS.
+      // Waits come only at the end of odd phases; the other barriers are bare
+      // (a __syncthreads() would also wait for the loads in flight and for the
+      // reads issued ahead of the next phase).
+      __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGEB];
+      constexpr int NPV = 2 * NKB * DB;     // P V MFMAs per tile and wave
+      constexpr int NQK = DCH * NKB;        // Q K^T MFMAs per tile and wave
+      constexpr int PP_AH = 4;              // operand reads ahead of their MFMA
+      f32x16 sc[NKB];                       // scores of the tile whose softmax is next
+      uint32_t pk[NKB][8];                  // its probabilities, 16 bit
+      u32x4 ab[NPV + NQK];                  // operand A of each MFMA of a matrix phase
+
+      // Wait for this wave's loads at the end of a phase (nothing moves across it).
+      auto pp_wait = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmem_all();
+      };
+      auto pp_bar = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // Operand A of MFMA n of a matrix phase: V^T of 16 keys by two transposing
+      // reads, or a 32-key block of K.
+      auto rd = [&](auto mode_c, int n, const uint8_t* vs, const uint8_t* ks) __attribute__((always_inline)) {
+        using O = PPOrder<decltype(mode_c)::value, PP_AH, NPV, NQK>;
+        const int i = O::idx(n);
+        if (O::kind(n) == 0) {
+          const int kc = i / DB, d = i % DB;
+          const uint8_t* vb = vs + kc * 16 * ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        }
+        const int c = i / NKB, kb = i % NKB;
+        return *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]);
+      };
+      // Reads of the first PP_AH operands of the next matrix phase (all V).
+      auto m_pre = [&](const uint8_t* vstage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < PP_AH; ++n) ab[n] = rd(ModeTag<PP_FULL>{}, n, vstage + GTILEB, nullptr);
+      };
+      // Matrix phase: P V from `vstage` with pk, then / interleaved with
+      // S^T = K Q^T from `kstage` into sc. PIN: the first reads are issued here.
+      auto m_phase = [&](auto mode_c, auto pin_c, const uint8_t* vstage, const uint8_t* kstage)
+          __attribute__((always_inline)) {
+        using O = PPOrder<decltype(mode_c)::value, PP_AH, NPV, NQK>;
+        constexpr bool PIN = decltype(pin_c)::value;
+        const uint8_t* vs = vstage + GTILEB;
+        if constexpr (PIN) {
+#pragma unroll
+          for (int n = 0; n < PP_AH; ++n) ab[n] = rd(mode_c, n, vs, kstage);
+        }
+#pragma unroll
+        for (int n = 0; n < O::total; ++n) {
+          if (n + PP_AH < O::total) ab[n + PP_AH] = rd(mode_c, n + PP_AH, vs, kstage);
+          const int i = O::idx(n);
+          if (O::kind(n) == 0) {
+            const int kc = i / DB, d = i % DB, kb = kc >> 1, e = kc & 1;
+            const u32x4 bop = {pk[kb][e * 4 + 0], pk[kb][e * 4 + 1], pk[kb][e * 4 + 2], pk[kb][e * 4 + 3]};
+            acc[d] = mfma32<BF16>(ab[n], bop, acc[d]);
+          } else {
+            const int c = i / NKB, kb = i % NKB;
+            sc[kb] = mfma32<BF16>(ab[n], qreg[c], c == 0 ? f32x16{} : sc[kb]);
+          }
+        }
+        if constexpr (PIN) __builtin_amdgcn_sched_group_barrier(0x100, O::reads_before(PP_AH), 0);
+        pp_groups<O, PP_AH, 0>();
+      };
+      // Vector phase: mask (diagonal and tail tiles), exponentials, row sums.
+      auto s_phase = [&](auto masked_c, auto first_c, int j) __attribute__((always_inline)) {
+        const int key0 = j * GBN;
+        if constexpr (decltype(masked_c)::value) {
+          if ((key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0)) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                const bool ok = (key < L) && (!CAUSAL || key <= qi);
+                sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+              }
+            }
+          }
+        }
+        if constexpr (decltype(first_c)::value) {
+          // every row sees key 0 of its first tile: the maximum is finite
+          float mx = sc[0][0];
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+          }
+          m_run = half_max(mx) * c_log2;
+        }
+        float tl = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * t], c_log2, -m_run));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * t + 1], c_log2, -m_run));
+            pk[kb][t] = pack2<BF16>(e0, e1);
+            if constexpr (BF16) {
+              tl += e0 + e1;
+            } else {
+              tl = add_pair_f16(pk[kb][t], tl);
+            }
+          }
+        }
+        if constexpr (!decltype(first_c)::value) bad |= __builtin_amdgcn_ballot_w64(!(tl <= OPT_LIMIT));
+        l_run += tl;
+        // Keep the packing in this phase (the compiler would sink it to the P V
+        // MFMAs, into the matrix phase).
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(pk[kb][t]));
+        }
+      };
+      const int n = n_kv - j_lo;            // tiles of this workgroup (>= 1)
+      // Tiles [0, n_pl) need no mask. Plain steps t = 1 .. t_pe - 1 (a multiple of
+      // three of them, so the masked loop starts on the same stage rotation), all
+      // before the last step.
+      int n_pl = min(n_kv, L / GBN);
+      if (CAUSAL) n_pl = min(n_pl, (q0 + 1) / GBN);
+      n_pl -= j_lo;
+      const int t_pe = 1 + max(0, min(n_pl, n - 1) - 1) / 3 * 3;
+
+      // The schedule is compiled once per wave group, so that no branch on the
+      // group sits between a load and its wait (the compiler would then assume
+      // the other group's loads in flight and wait for them before LDS reads).
+      auto schedule = [&](auto late_c) __attribute__((always_inline)) {
+        constexpr bool LATE = decltype(late_c)::value;
+        // One step: S(t), then M(t+1) (LAST: P V of tile t alone, no barrier after
+        // it for waves 4-7, whose last phase it is). Stages: V of tile t in vst,
+        // K of tile t+1 in kst, tile t+2 goes into ist.
+        auto step = [&](auto masked_c, auto first_c, auto last_c, int t, const uint8_t* vst,
+                        const uint8_t* kst, uint8_t* ist) __attribute__((always_inline)) {
+          constexpr bool LAST = decltype(last_c)::value;
+          constexpr bool SKIP = decltype(masked_c)::value && CAUSAL;
+          const int j = j_lo + t;
+          // Under causality a wave none of whose rows sees a key of tile t skips
+          // its softmax, Q K^T and P V (and those of every later tile).
+          const bool act0 = !(SKIP && j * GBN > wq0 + 31);
+          const bool act1 = !LAST && !(SKIP && (j + 1) * GBN > wq0 + 31);
+          if (!LAST && LATE && t + 2 < n) issue_to(j + 2, ist);     // phase 2t+2 of waves 4-7
+          if (act0) {
+            s_phase(masked_c, first_c, j);
+            m_pre(vst);
+          }
+          if constexpr (!LATE) pp_wait();                           // end of phase 2t+1
+          pp_bar();
+          if (!LAST && !LATE && t + 2 < n) issue_to(j + 2, ist);    // phase 2t+2 of waves 0-3
+          if (act1) {
+            m_phase(ModeTag<PP_FULL>{}, BoolTag<false>{}, vst, kst);
+          } else if (act0) {
+            m_phase(ModeTag<PP_PV>{}, BoolTag<false>{}, vst, vst);
+          }
+          if constexpr (LATE) pp_wait();                            // end of phase 2t+3
+          if constexpr (!LAST || !LATE) pp_bar();
+        };
+        // Phase 0 (1 for waves 4-7): Q K^T of tile 0, whose loads the barrier
+        // above waited for; tile 1 goes out at the start of phase 0.
+        if (n > 1) issue_to(j_lo + 1, smem1);
+        if constexpr (LATE) pp_bar();
+        m_phase(ModeTag<PP_QK>{}, BoolTag<true>{}, smem0, smem0);
+        if constexpr (LATE) pp_wait();
+        pp_bar();
+        if (n == 1) {
+          step(masked_t, BoolTag<true>{}, BoolTag<true>{}, 0, smem0, smem0, smem0);
+        } else {
+          step(masked_t, BoolTag<true>{}, BoolTag<false>{}, 0, smem0, smem1, smem2);
 #pragma unroll 1
-    for (int j = j_lo + 1; j < j_plain; j += 2) {
-      issue_tile(j + 1, 0);
-      compute_tile(plain_t, ModeTag<TILE_FAST>{}, j, smem1);
-      wait_vmem_all();
-      __syncthreads();
-      if (j + 2 < n_kv) issue_tile(j + 2, 1);
-      compute_tile(plain_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
-      wait_vmem_all();
-      __syncthreads();
-    }
+          for (int t = 1; t < t_pe; t += 3) {
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t, smem1, smem2, smem0);
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, smem2, smem0, smem1);
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, smem0, smem1, smem2);
+          }
 #pragma unroll 1
-    for (int j = j_plain; j < n_kv; j += 2) {
-      if (j + 1 < n_kv) issue_tile(j + 1, 0);
-      compute_tile(masked_t, ModeTag<TILE_FAST>{}, j, smem1);
+          for (int t = t_pe; t < n - 1; t += 3) {
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t, smem1, smem2, smem0);
+            if (t + 1 >= n - 1) break;
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, smem2, smem0, smem1);
+            if (t + 2 >= n - 1) break;
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, smem0, smem1, smem2);
+          }
+          // The last step: no loads are in flight any more, so its stage may be
+          // chosen at run time.
+          const int sl = (n - 1) % 3;
+          const uint8_t* vl = sl == 0 ? smem0 : (sl == 1 ? smem1 : smem2);
+          step(masked_t, BoolTag<false>{}, BoolTag<true>{}, n - 1, vl, vl, nullptr);
+        }
+      };
+      if (wave >= 4) {
+        schedule(BoolTag<true>{});
+      } else {
+        schedule(BoolTag<false>{});
+      }
+    } else {
+      // Tiles before j_plain hold no key that any row of the workgroup must not
+      // see: they run without the mask code, in a loop of their own (a branch
+      // between the two kinds inside one loop makes the compiler copy the
+      // accumulators at every join). Their count after the first tile is kept
+      // even so that the masked loop always starts on stage 1.
+      int j_plain = min(n_kv, L / GBN);
+      if (CAUSAL) j_plain = min(j_plain, (q0 + 1) / GBN);
+      j_plain = j_lo + 1 + (max(0, j_plain - (j_lo + 1)) & ~1);
+      // First tile: row maxima, the reference of the optimistic tiles after it.
+      if (j_lo + 1 < n_kv) issue_tile(j_lo + 1, 1);
+      compute_tile(masked_t, ModeTag<TILE_FIRST>{}, j_lo, smem0);
       wait_vmem_all();
       __syncthreads();
-      if (j + 1 >= n_kv) break;
-      if (j + 2 < n_kv) issue_tile(j + 2, 1);
-      compute_tile(masked_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
-      wait_vmem_all();
-      __syncthreads();
+#pragma unroll 1
+      for (int j = j_lo + 1; j < j_plain; j += 2) {
+        issue_tile(j + 1, 0);
+        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j, smem1);
+        wait_vmem_all();
+        __syncthreads();
+        if (j + 2 < n_kv) issue_tile(j + 2, 1);
+        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+        wait_vmem_all();
+        __syncthreads();
+      }
+#pragma unroll 1
+      for (int j = j_plain; j < n_kv; j += 2) {
+        if (j + 1 < n_kv) issue_tile(j + 1, 0);
+        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j, smem1);
+        wait_vmem_all();
+        __syncthreads();
+        if (j + 1 >= n_kv) break;
+        if (j + 2 < n_kv) issue_tile(j + 2, 1);
+        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+        wait_vmem_all();
+        __syncthreads();
+      }
     }
     // Some tile of some wave exceeded the bound (its maximum grew by more than
     // log2(OPT_LIMIT) over the first tile's): the whole workgroup walks its keys
