@@ -257,6 +257,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
     // P^T = exp2(s * c - lse2), dS^T = P^T (dP^T - delta), packed to 16 bit.
     const bool need_mask = MASKED && ((key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0));
+    // Register r of block kb holds key key0 + 4 hh + c, c = 32 kb + 8 (r / 4) + r % 4
+    // (a constant): visible iff key < L and, causal, key <= qi, i.e. c <= T.
+    const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
     uint32_t pk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -267,10 +270,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * t + e;
           float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c_log2, -lse2));
-          if (need_mask) {
-            const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            if (!(key < L && (!CAUSAL || key <= qi))) pr = 0.0f;
-          }
+          if (need_mask && !(kb * 32 + (r >> 2) * 8 + (r & 3) <= T)) pr = 0.0f;
           ds[e] = pr * (dp[kb][r] - delta);
         }
         pk[kb][t] = pack2<BF16>(ds[0], ds[1]);

@@ -206,13 +206,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
 
     const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0);
     if (need_mask) {
+      // Register r of block kb holds key key0 + 4 hh + c, c = 32 kb + 8 (r / 4) + r % 4
+      // (a constant): visible iff key < L and, causal, key <= qi, i.e. c <= T.
+      const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-          const bool ok = (key < L) && (!CAUSAL || key <= qi);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          s[kb][r] = c <= T ? s[kb][r] : -INFINITY;
         }
       }
     }

@@ -401,13 +401,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         }
       }
     } else if (need_mask) {
+      // Register r of block kb holds key key0 + 4 hh + c, c = 32 kb + 8 (r / 4) + r % 4
+      // (a constant): visible iff key < L and, causal, key <= qi, i.e. c <= T.
+      const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-          const bool ok = (key < L) && (!CAUSAL || key <= qi);
-          s[kb][r] = ok ? s[kb][r] : -INFINITY;
+          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+          s[kb][r] = c <= T ? s[kb][r] : -INFINITY;
         }
       }
     }
@@ -630,13 +632,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         const int key0 = j * GBN;
         if constexpr (decltype(masked_c)::value) {
           if ((key0 + BN > L) || (CAUSAL && key0 + BN - 1 > wq0)) {
+            // key key0 + 4 hh + c is visible iff c <= T (as in compute_tile)
+            const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
-                const int key = key0 + kb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                const bool ok = (key < L) && (!CAUSAL || key <= qi);
-                sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+                sc[kb][r] = c <= T ? sc[kb][r] : -INFINITY;
               }
             }
           }
