@@ -87,6 +87,9 @@ template <class O, int AH, int N> __device__ __forceinline__ void pp_groups() {
   }
 }
 
+// One stage of an LDS ring: where a key tile's K rows and V rows go.
+struct Stage { uint8_t* k; uint8_t* v; };
+
 // acc + lo(p) + hi(p) for a pair of fp16 values (one v_dot2).
 __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
   const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -126,13 +129,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   __shared__ __attribute__((aligned(1024))) uint8_t smem0[STAGEB];
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
   __shared__ int redo_flag;     // some wave saw a probability above OPT_LIMIT
+  // The three-stage ring of the ping-pong instances keeps K and V tiles in
+  // arrays of their own, the K tiles below 48 KB and the V tiles above: every
+  // read of either kind then reaches all three stages from one register of lane
+  // offsets plus the instruction's 16-bit immediate offset (with 32 KB stages the
+  // third one starts at 64 KB, past that offset, and its reads needed address
+  // arithmetic and registers of their own).
+  __shared__ __attribute__((aligned(1024))) uint8_t pk0[GTILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t pk1[GTILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t pk2[GTILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t pv0[GTILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t pv1[GTILEB];
+  __shared__ __attribute__((aligned(1024))) uint8_t pv2[GTILEB];
   // The 8-wave D = 128 plain instances run the ping-pong schedule (below) on a
   // three-stage ring.
   constexpr bool PINGPONG = !EXT && KS == 1 && NW == 8 && D == 128;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Wave-uniform: the LDS addresses of the direct loads are then scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 31;     // query row inside the wave / MFMA row index
   const int hh = lane >> 5;     // which half of the contraction this lane feeds
   const int wr = KS == 1 ? wave : wave % NWR;   // which 32 query rows of the tile
@@ -260,14 +276,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     }
   }
 
+  // The ring's stages (the ping-pong instances: three, in the arrays above).
+  const Stage st0 = PINGPONG ? Stage{pk0, pv0} : Stage{smem0, smem0 + GTILEB};
+  const Stage st1 = PINGPONG ? Stage{pk1, pv1} : Stage{smem1, smem1 + GTILEB};
+  const Stage st2 = {pk2, pv2};
+
   // Issue the direct loads of key tile j into `stage` (K tile, then V tile).
-  auto issue_to = [&](int j, uint8_t* stage) {
+  auto issue_to = [&](int j, const Stage& stage) {
     const int key0 = j * GBN;
     const uint32_t rows = (uint32_t)min(L - key0, GBN);
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kg + (size_t)key0 * p.H * D, rows * tok_bytes);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vg + (size_t)key0 * p.H * D, rows * tok_bytes);
-    uint8_t* kdst = stage + wave * LDW * 1024;
-    uint8_t* vdst = kdst + GTILEB;
+    uint8_t* kdst = stage.k + wave * LDW * 1024;
+    uint8_t* vdst = stage.v + wave * LDW * 1024;
 #pragma unroll
     for (int u = 0; u < LDW; ++u) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vdst + u * 1024), 16, (int)ld_voff[u], 0, 0, 0);
     }
   };
-  auto issue_tile = [&](int j, int st) { issue_to(j, st ? smem1 : smem0); };
+  auto issue_tile = [&](int j, int st) { issue_to(j, st ? st1 : st0); };
 
   // ---- running statistics and accumulator --------------------------------
   f32x16 acc[DB];
@@ -303,11 +324,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   //   TILE_FIRST: a wave's first tile when each of its rows sees a key of it:
   //              the row maximum becomes the running maximum (the accumulator
   //              and the sum are still zero), again with no branch.
-  auto compute_tile = [&](auto masked_c, auto mode_c, int j, const uint8_t* stage) {
+  auto compute_tile = [&](auto masked_c, auto mode_c, int j, const Stage& stage) {
     constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int MODE = decltype(mode_c)::value;
-    const uint8_t* ks = stage + kgrp * TILEB;
-    const uint8_t* vs = stage + GTILEB + kgrp * TILEB;
+    const uint8_t* ks = stage.k + kgrp * TILEB;
+    const uint8_t* vs = stage.v + kgrp * TILEB;
     const int key0 = j * GBN + kgrp * BN;
     // A wave none of whose rows sees a key of this tile has nothing to do.
     if constexpr (MASKED) {
@@ -529,12 +550,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 #pragma unroll 1
     for (int j = j_lo; j < n_kv; j += 2) {
       if (j + 1 < n_kv) issue_tile(j + 1, 1);
-      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j, smem0);
+      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j, st0);
       wait_vmem_all();
       __syncthreads();
       if (j + 1 >= n_kv) break;
       if (j + 2 < n_kv) issue_tile(j + 2, 0);
-      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j + 1, smem1);
+      compute_tile(masked_t, ModeTag<TILE_OPT>{}, j + 1, st1);
       wait_vmem_all();
       __syncthreads();
     }
@@ -559,7 +580,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       // Waits come only at the end of odd phases; the other barriers are bare
       // (a __syncthreads() would also wait for the loads in flight and for the
       // reads issued ahead of the next phase).
-      __shared__ __attribute__((aligned(1024))) uint8_t smem2[STAGEB];
       constexpr int NPV = 2 * NKB * DB;     // P V MFMAs per tile and wave
       constexpr int NQK = DCH * NKB;        // Q K^T MFMAs per tile and wave
       constexpr int PP_AH = 4;              // operand reads ahead of their MFMA
@@ -581,14 +601,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       };
       // Operand A of MFMA n of a matrix phase: V^T of 16 keys by two transposing
       // reads, or a 32-key block of K.
+      // V reads: lane offsets carry a 48 KB bias the compiler cannot see through,
+      // so that the V stages (above 48 KB) are reached by immediate offsets.
+      constexpr int VBIAS = 3 * GTILEB;
+      uint32_t v_offb[2][DB];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          v_offb[t2][d] = v_off[t2][d] + VBIAS;
+          asm volatile("" : "+v"(v_offb[t2][d]));
+        }
+      }
       auto rd = [&](auto mode_c, int n, const uint8_t* vs, const uint8_t* ks) __attribute__((always_inline)) {
         using O = PPOrder<decltype(mode_c)::value, PP_AH, NPV, NQK>;
         const int i = O::idx(n);
         if (O::kind(n) == 0) {
           const int kc = i / DB, d = i % DB;
-          const uint8_t* vb = vs + kc * 16 * ROWB;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
+          const uint8_t* vb = vs - VBIAS + kc * 16 * ROWB;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_offb[0][d]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_offb[1][d]));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
@@ -596,24 +628,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         return *reinterpret_cast<const u32x4*>(ks + kb * 32 * ROWB + k_off[c]);
       };
       // Reads of the first PP_AH operands of the next matrix phase (all V).
-      auto m_pre = [&](const uint8_t* vstage) __attribute__((always_inline)) {
+      auto m_pre = [&](const Stage& vstage) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < PP_AH; ++n) ab[n] = rd(ModeTag<PP_FULL>{}, n, vstage + GTILEB, nullptr);
+        for (int n = 0; n < PP_AH; ++n) ab[n] = rd(ModeTag<PP_FULL>{}, n, vstage.v, nullptr);
       };
       // Matrix phase: P V from `vstage` with pk, then / interleaved with
       // S^T = K Q^T from `kstage` into sc. PIN: the first reads are issued here.
-      auto m_phase = [&](auto mode_c, auto pin_c, const uint8_t* vstage, const uint8_t* kstage)
+      auto m_phase = [&](auto mode_c, auto pin_c, const Stage& vstage, const Stage& kstage)
           __attribute__((always_inline)) {
         using O = PPOrder<decltype(mode_c)::value, PP_AH, NPV, NQK>;
         constexpr bool PIN = decltype(pin_c)::value;
-        const uint8_t* vs = vstage + GTILEB;
+        const uint8_t* vs = vstage.v;
+        const uint8_t* ks = kstage.k;
         if constexpr (PIN) {
 #pragma unroll
-          for (int n = 0; n < PP_AH; ++n) ab[n] = rd(mode_c, n, vs, kstage);
+          for (int n = 0; n < PP_AH; ++n) ab[n] = rd(mode_c, n, vs, ks);
         }
 #pragma unroll
         for (int n = 0; n < O::total; ++n) {
-          if (n + PP_AH < O::total) ab[n + PP_AH] = rd(mode_c, n + PP_AH, vs, kstage);
+          if (n + PP_AH < O::total) ab[n + PP_AH] = rd(mode_c, n + PP_AH, vs, ks);
           const int i = O::idx(n);
           if (O::kind(n) == 0) {
             const int kc = i / DB, d = i % DB, kb = kc >> 1, e = kc & 1;
@@ -696,8 +729,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         // One step: S(t), then M(t+1) (LAST: P V of tile t alone, no barrier after
         // it for waves 4-7, whose last phase it is). Stages: V of tile t in vst,
         // K of tile t+1 in kst, tile t+2 goes into ist.
-        auto step = [&](auto masked_c, auto first_c, auto last_c, int t, const uint8_t* vst,
-                        const uint8_t* kst, uint8_t* ist) __attribute__((always_inline)) {
+        auto step = [&](auto masked_c, auto first_c, auto last_c, int t, const Stage& vst,
+                        const Stage& kst, const Stage& ist) __attribute__((always_inline)) {
           constexpr bool LAST = decltype(last_c)::value;
           constexpr bool SKIP = decltype(masked_c)::value && CAUSAL;
           const int j = j_lo + t;
@@ -726,34 +759,34 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         };
         // Phase 0 (1 for waves 4-7): Q K^T of tile 0, whose loads the barrier
         // above waited for; tile 1 goes out at the start of phase 0.
-        if (n > 1) issue_to(j_lo + 1, smem1);
+        if (n > 1) issue_to(j_lo + 1, st1);
         if constexpr (LATE) pp_bar();
-        m_phase(ModeTag<PP_QK>{}, BoolTag<true>{}, smem0, smem0);
+        m_phase(ModeTag<PP_QK>{}, BoolTag<true>{}, st0, st0);
         if constexpr (LATE) pp_wait();
         pp_bar();
         if (n == 1) {
-          step(masked_t, BoolTag<true>{}, BoolTag<true>{}, 0, smem0, smem0, smem0);
+          step(masked_t, BoolTag<true>{}, BoolTag<true>{}, 0, st0, st0, st0);
         } else {
-          step(masked_t, BoolTag<true>{}, BoolTag<false>{}, 0, smem0, smem1, smem2);
+          step(masked_t, BoolTag<true>{}, BoolTag<false>{}, 0, st0, st1, st2);
 #pragma unroll 1
           for (int t = 1; t < t_pe; t += 3) {
-            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t, smem1, smem2, smem0);
-            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, smem2, smem0, smem1);
-            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, smem0, smem1, smem2);
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t, st1, st2, st0);
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, st2, st0, st1);
+            step(plain_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, st0, st1, st2);
           }
 #pragma unroll 1
           for (int t = t_pe; t < n - 1; t += 3) {
-            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t, smem1, smem2, smem0);
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t, st1, st2, st0);
             if (t + 1 >= n - 1) break;
-            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, smem2, smem0, smem1);
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 1, st2, st0, st1);
             if (t + 2 >= n - 1) break;
-            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, smem0, smem1, smem2);
+            step(masked_t, BoolTag<false>{}, BoolTag<false>{}, t + 2, st0, st1, st2);
           }
           // The last step: no loads are in flight any more, so its stage may be
           // chosen at run time.
           const int sl = (n - 1) % 3;
-          const uint8_t* vl = sl == 0 ? smem0 : (sl == 1 ? smem1 : smem2);
-          step(masked_t, BoolTag<false>{}, BoolTag<true>{}, n - 1, vl, vl, nullptr);
+          const Stage vl = sl == 0 ? st0 : (sl == 1 ? st1 : st2);
+          step(masked_t, BoolTag<false>{}, BoolTag<true>{}, n - 1, vl, vl, vl);
         }
       };
       if (wave >= 4) {
@@ -772,29 +805,29 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       j_plain = j_lo + 1 + (max(0, j_plain - (j_lo + 1)) & ~1);
       // First tile: row maxima, the reference of the optimistic tiles after it.
       if (j_lo + 1 < n_kv) issue_tile(j_lo + 1, 1);
-      compute_tile(masked_t, ModeTag<TILE_FIRST>{}, j_lo, smem0);
+      compute_tile(masked_t, ModeTag<TILE_FIRST>{}, j_lo, st0);
       wait_vmem_all();
       __syncthreads();
 #pragma unroll 1
       for (int j = j_lo + 1; j < j_plain; j += 2) {
         issue_tile(j + 1, 0);
-        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j, smem1);
+        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j, st1);
         wait_vmem_all();
         __syncthreads();
         if (j + 2 < n_kv) issue_tile(j + 2, 1);
-        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+        compute_tile(plain_t, ModeTag<TILE_FAST>{}, j + 1, st0);
         wait_vmem_all();
         __syncthreads();
       }
 #pragma unroll 1
       for (int j = j_plain; j < n_kv; j += 2) {
         if (j + 1 < n_kv) issue_tile(j + 1, 0);
-        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j, smem1);
+        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j, st1);
         wait_vmem_all();
         __syncthreads();
         if (j + 1 >= n_kv) break;
         if (j + 2 < n_kv) issue_tile(j + 2, 1);
-        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j + 1, smem0);
+        compute_tile(masked_t, ModeTag<TILE_FAST>{}, j + 1, st0);
         wait_vmem_all();
         __syncthreads();
       }
@@ -815,7 +848,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
         issue_tile(j, 0);
         wait_vmem_all();
         __syncthreads();
-        compute_tile(masked_t, ModeTag<TILE_MAX>{}, j, smem0);
+        compute_tile(masked_t, ModeTag<TILE_MAX>{}, j, st0);
         __syncthreads();
       }
     }
