@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[STAGEB];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
   const int li = lane & 31;
   const int hh = lane >> 5;
 
