@@ -147,8 +147,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  // Wave-uniform: the LDS addresses of the direct loads are then scalar.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Ping-pong instances: wave-uniform, so that the LDS addresses of the direct
+  // loads are scalar. (In the D = 64 8-wave instances the scalar form raised
+  // the registers from 126 to 154, past two workgroups per CU.)
+  const int wave = PINGPONG ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int li = lane & 31;     // query row inside the wave / MFMA row index
   const int hh = lane >> 5;     // which half of the contraction this lane feeds
   const int wr = KS == 1 ? wave : wave % NWR;   // which 32 query rows of the tile
