@@ -264,6 +264,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   // at key row (s / 4) of a 4-key group and at a 4-column group; the read
   // hands lane i the 4 keys of column (group(i/4) + i%4). Column groups are
   // ordered so that output rows come out as runs of 8 consecutive columns.
+  // Ping-pong instances: the V stages lie above 48 KB (see the arrays); the lane
+  // offsets carry that bias so that every V read is register + immediate offset.
+  constexpr int VBIAS = PINGPONG ? 3 * GTILEB : 0;
   uint32_t v_off[2][DB];
   {
     const int blk = li >> 4, s = li & 15;
@@ -273,7 +276,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int col = db * 32 + blk * 16 + swap23(4 * (s & 3));
-        v_off[t2][db] = key * ROWB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) * 2));
+        v_off[t2][db] = key * ROWB + ((((col >> 3) ^ swz<D>(key)) << 4) | ((col & 7) * 2)) + VBIAS;
+        // Ping-pong: the bias must stay in the register (the compiler would fold it
+        // back into the stage address, past the immediate-offset range).
+        if constexpr (PINGPONG) asm volatile("" : "+v"(v_off[t2][db]));
       }
     }
   }
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       const u32x4 bop = {pk[kb][e * 4 + 0], pk[kb][e * 4 + 1], pk[kb][e * 4 + 2], pk[kb][e * 4 + 3]};
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        const uint8_t* vb = vs + kc * 16 * ROWB;
+        const uint8_t* vb = vs - VBIAS + kc * 16 * ROWB;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
@@ -603,26 +609,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
       };
       // Operand A of MFMA n of a matrix phase: V^T of 16 keys by two transposing
       // reads, or a 32-key block of K.
-      // V reads: lane offsets carry a 48 KB bias the compiler cannot see through,
-      // so that the V stages (above 48 KB) are reached by immediate offsets.
-      constexpr int VBIAS = 3 * GTILEB;
-      uint32_t v_offb[2][DB];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          v_offb[t2][d] = v_off[t2][d] + VBIAS;
-          asm volatile("" : "+v"(v_offb[t2][d]));
-        }
-      }
       auto rd = [&](auto mode_c, int n, const uint8_t* vs, const uint8_t* ks) __attribute__((always_inline)) {
         using O = PPOrder<decltype(mode_c)::value, PP_AH, NPV, NQK>;
         const int i = O::idx(n);
         if (O::kind(n) == 0) {
           const int kc = i / DB, d = i % DB;
           const uint8_t* vb = vs - VBIAS + kc * 16 * ROWB;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_offb[0][d]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_offb[1][d]));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[0][d]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + v_off[1][d]));
           const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
           return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
@@ -737,15 +731,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
           constexpr bool SKIP = decltype(masked_c)::value && CAUSAL;
           const int j = j_lo + t;
           // Under causality a wave none of whose rows sees a key of tile t skips
-          // the P V of tile t and the Q K^T of tile t+1 (and every later matrix
-          // phase; the Q K^T of the first tile it does not see is still computed).
-          // Its softmax phases still run, on all-masked scores: skipping them too
-          // made the joins spill 27 registers (measured: 57 MB more writes and
-          // 104 MB more reads of HBM per LLaMA-shaped launch).
+          // the softmax of tile t, the P V of tile t and the Q K^T of tile t+1 (and
+          // every later phase; the Q K^T of the first tile it does not see is still
+          // computed): its scores there are all masked, so they would add nothing.
+          // It still takes every barrier.
           const bool act0 = !(SKIP && j * GBN > wq0 + 31);
           if (!LAST && LATE && t + 2 < n) issue_to(j + 2, ist);     // phase 2t+2 of waves 4-7
-          s_phase(masked_c, first_c, j);
-          m_pre(vst);
+          if (act0) {
+            s_phase(masked_c, first_c, j);
+            m_pre(vst);
+          }
           if constexpr (!LATE) pp_wait();                           // end of phase 2t+1
           pp_bar();
           if (!LAST && !LATE && t + 2 < n) issue_to(j + 2, ist);    // phase 2t+2 of waves 0-3
