@@ -141,6 +141,26 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                  const float* alibi_slopes, void* stream);
 
 /*
+ * attn_fwd_ext_tuned -- attn_fwd_ext with its launch shape fixed by the caller
+ * (for tests that must reach every kernel instance, and for sweeps).
+ *
+ * Same arguments, layouts, semantics and errors as attn_fwd_ext, plus:
+ *   tile_rows  : 0 lets the library choose as attn_fwd_ext does; 128 runs the
+ *                4-wave mask-variant kernel; 256 runs the 8-wave ping-pong
+ *                kernel, which takes the ALiBi bias alone: it needs D == 128,
+ *                window == n_global == 0 and alibi_slopes != NULL. Anything
+ *                else: ATTN_ERR_UNSUPPORTED.
+ *   head_group : as in attn_fwd_tuned (0: the library's choice; negative:
+ *                ATTN_ERR_SHAPE).
+ * The two kernels agree to rounding (they sum a row's keys in the same order
+ * but take the running maximum at different steps).
+ */
+int attn_fwd_ext_tuned(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int H, int S, int D, int causal, float scale, int dtype,
+                       const int32_t* cu_seqlens, int window, int n_global,
+                       const float* alibi_slopes, int tile_rows, int head_group, void* stream);
+
+/*
  * attn_fwd_fp8 -- attn_fwd on FP8 inputs.
  *
  * jianying88.com/news/49672 §3 mentions FP8 attention (less memory, a small

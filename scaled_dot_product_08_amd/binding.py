@@ -19,7 +19,7 @@ STATUS = {
     -7: "ATTN_ERR_SEQLENS", -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WORKSPACE",
     -10: "ATTN_ERR_SCRATCH",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
+EXPORTS = ("attn_fwd", "attn_fwd_tuned", "attn_fwd_ext", "attn_fwd_ext_tuned", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_size", "attn_decode",
            "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror", "attn_check_cu_seqlens", "attn_version",
            "attn_last_hip_error", "attn_clock_sample")
 
@@ -64,6 +64,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.attn_fwd_ext.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
         [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
          ctypes.c_void_p]
+    lib.attn_fwd_ext_tuned.restype = ctypes.c_int
+    lib.attn_fwd_ext_tuned.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + \
+        [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_fp8.restype = ctypes.c_int
     lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float] * 4 + \
         [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -151,6 +155,15 @@ def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, 
     return load_library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H), int(S),
                                        int(D), int(causal), float(scale), int(dtype), cu_ptr,
                                        int(window), int(n_global), alibi_ptr, stream_ptr)
+
+
+def attn_fwd_ext_tuned_raw(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, B, H, S, D, causal, scale, dtype,
+                           cu_ptr, window, n_global, alibi_ptr, tile_rows, head_group, stream_ptr) -> int:
+    """Direct call of attn_fwd_ext_tuned with integer pointers; returns the status code."""
+    return load_library().attn_fwd_ext_tuned(q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr, int(B), int(H),
+                                             int(S), int(D), int(causal), float(scale), int(dtype),
+                                             cu_ptr, int(window), int(n_global), alibi_ptr,
+                                             int(tile_rows), int(head_group), stream_ptr)
 
 
 def attn_decode_raw(q_ptr, k_ptr, v_ptr, seqlens_ptr, out_ptr, lse_ptr, B, H, Sq, S_max, D, causal,
@@ -280,9 +293,9 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
     lse_ptr = None if lse is None else lse.data_ptr()
     masks = bool(window or n_global or alibi_slopes is not None)
     tuned = bool(tile_rows or key_split or head_group)
-    if masks and tuned:
-        raise ValueError("the mask/bias variants take no launch-shape arguments")
-    if tuned:
+    if masks and key_split:
+        raise ValueError("the mask/bias variants take no key_split argument")
+    if tuned and not masks:
         st = attn_fwd_tuned_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                                 B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
                                 tile_rows, key_split, head_group, _stream_ptr(stream))
@@ -294,9 +307,15 @@ def attn_fwd(q, k, v, out, lse=None, *, causal: bool, scale: float | None = None
                 raise ValueError("alibi_slopes must be a contiguous float32 tensor of H slopes "
                                  "on q's device")
             al = alibi_slopes.data_ptr()
-        st = attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
-                              B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
-                              window, n_global, al, _stream_ptr(stream))
+        if tuned:
+            st = attn_fwd_ext_tuned_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                        lse_ptr, B, H, S, D, int(bool(causal)), scale,
+                                        _dtype_code(q), cu_ptr, window, n_global, al, tile_rows,
+                                        head_group, _stream_ptr(stream))
+        else:
+            st = attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                  B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,
+                                  window, n_global, al, _stream_ptr(stream))
     else:
         st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                           B, H, S, D, int(bool(causal)), scale, _dtype_code(q), cu_ptr,

@@ -230,6 +230,24 @@ int attn_fwd_ext(const void* q, const void* k, const void* v, void* out, float* 
                     n_global, alibi_slopes, sdpa08::FwdTuning{}, stream);
 }
 
+int attn_fwd_ext_tuned(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int H, int S, int D, int causal, float scale, int dtype,
+                       const int32_t* cu_seqlens, int window, int n_global,
+                       const float* alibi_slopes, int tile_rows, int head_group, void* stream) {
+  if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256) return ATTN_ERR_UNSUPPORTED;
+  if (tile_rows == 256 && (window != 0 || n_global != 0 || alibi_slopes == nullptr || D != 128)) {
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (head_group < 0) return ATTN_ERR_SHAPE;
+  if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4)) return ATTN_ERR_ALIGN;
+  sdpa08::FwdTuning t;
+  t.tile_rows = tile_rows;
+  t.key_split = 1;
+  t.head_group = head_group;
+  return fwd_common(q, k, v, out, lse, B, H, S, D, causal, scale, dtype, cu_seqlens, window,
+                    n_global, alibi_slopes, t, stream);
+}
+
 size_t attn_decode_workspace_size(int B, int H, int Sq, int S_max, int D, int num_splits) {
   if (B < 0 || H < 1 || Sq < 0 || S_max < 0 || num_splits < 0 || (D != 64 && D != 128)) return 0;
   // Sized for the ragged plan, which has at least as many splits as the

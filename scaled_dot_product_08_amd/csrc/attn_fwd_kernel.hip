@@ -101,7 +101,10 @@ __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
 // maximum, row sum, accumulator) are merged through LDS at the end. It doubles
 // the waves per query tile, so problems with few tiles fill the chip in whole
 // rounds instead of leaving a half-empty last round.
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS>
+//
+// AB: the ALiBi bias alone (no window, no global rows) on the ping-pong
+// schedule; the other mask variants take EXT (4 waves).
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS, bool AB = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) {
   constexpr int NWAVES = NW;
   constexpr int NWR = NW / KS;                 // waves per key group (one per 32 query rows)
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   const int n_glob = EXT ? p.n_global : 0;
   const bool w_any_glob = EXT && wq0 < n_glob;          // some row of the wave is global
   const bool w_all_glob = EXT && wq0 + 31 < n_glob;     // every row of the wave is global
-  const float slope2 = (EXT && p.alibi != nullptr) ? p.alibi[h] * 1.4426950408889634f : 0.0f;
-  const bool use_alibi = EXT && p.alibi != nullptr;
+  const float slope2 = ((EXT || AB) && p.alibi != nullptr) ? p.alibi[h] * 1.4426950408889634f : 0.0f;
+  const bool use_alibi = AB || (EXT && p.alibi != nullptr);
   const uint32_t q_rows = (uint32_t)min(L - q0, BM);
 
   // ---- Q^T operand, resident in registers for the whole key loop ----------
@@ -320,6 +323,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   // first tile's row maximum is finite and serves as the reference for the rest.
   constexpr bool FAST_LOOP = !EXT && KS == 1;
 
+  // ALiBi in the log2-scaled domain: t = s * c - slope * |i - j| for the scores
+  // of a tile starting at key key0. slope * (j - i) = slope * (key0 + 4 hh - i)
+  // + slope * (offset of the register), and -|x| = min(x, -x).
+  auto alibi_bias = [&](f32x16 (&sv)[NKB], int key0) __attribute__((always_inline)) {
+    const float bl = slope2 * (float)(key0 + hh * 4 - qi);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float u = fmaf(slope2, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), bl);
+        sv[kb][r] = fmaf(sv[kb][r], c_log2, fminf(u, -u));
+      }
+    }
+  };
+
   // One key tile. MASKED (compile time): the tile may hold keys some row of the
   // workgroup must not see (diagonal, sequence end, mask variants); without it
   // the mask code is left out. MODE (compile time) picks the softmax scheme:
@@ -401,18 +419,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     if constexpr (EXT) {
       const bool glob_row = qi < n_glob;
       if (use_alibi) {
-        // Work in the log2-scaled domain: t = s * c - slope * |i - j|.
-        // slope * (j - i) = slope * (key0 + 4 hh - i) + slope * (offset of
-        // the register), and -|x| = min(x, -x).
-        const float bl = slope2 * (float)(key0 + hh * 4 - qi);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float u = fmaf(slope2, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), bl);
-            s[kb][r] = fmaf(s[kb][r], c_log2, fminf(u, -u));
-          }
-        }
+        alibi_bias(s, key0);
       }
       if (need_mask) {
 #pragma unroll
@@ -429,22 +436,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
           }
         }
       }
-    } else if (need_mask) {
-      // Register r of block kb holds key key0 + 4 hh + c, c = 32 kb + 8 (r / 4) + r % 4
-      // (a constant): visible iff key < L and, causal, key <= qi, i.e. c <= T.
-      const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
+    } else {
+      if constexpr (AB) alibi_bias(s, key0);
+      if (need_mask) {
+        // Register r of block kb holds key key0 + 4 hh + c, c = 32 kb + 8 (r / 4) + r % 4
+        // (a constant): visible iff key < L and, causal, key <= qi, i.e. c <= T.
+        const int T = (CAUSAL ? min(L - 1, qi) : L - 1) - key0 - hh * 4;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-          s[kb][r] = c <= T ? s[kb][r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+            s[kb][r] = c <= T ? s[kb][r] : -INFINITY;
+          }
         }
       }
     }
 
     // With ALiBi the scores are already log2-scaled.
-    const bool prescaled = EXT && use_alibi;
+    const bool prescaled = (EXT || AB) && use_alibi;
     const float c_mul = prescaled ? 1.0f : c_log2;
     // P = exp2(s * c - m), packed to 16 bit for P V; returns this lane's half
     // of the tile's row sum.
@@ -674,7 +684,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
           }
         }
         if constexpr (decltype(first_c)::value) {
-          // every row sees key 0 of its first tile: the maximum is finite
+          // every row sees key 0 of its first tile: the maximum is finite. With
+          // ALiBi it is taken over the unbiased scores: the bias is never
+          // positive and is zero at the row's own key, so this bounds every
+          // biased score of the tile, and later tiles (whose scores rise toward
+          // the diagonal only through the bias) stay within the optimistic bound
+          // as often as without it.
           float mx = sc[0][0];
 #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
@@ -683,13 +698,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
           }
           m_run = half_max(mx) * c_log2;
         }
+        if constexpr (AB) alibi_bias(sc, key0);      // scores now log2-scaled
         float tl = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * t], c_log2, -m_run));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][2 * t + 1], c_log2, -m_run));
+            const float e0 = __builtin_amdgcn_exp2f(AB ? sc[kb][2 * t] - m_run : fmaf(sc[kb][2 * t], c_log2, -m_run));
+            const float e1 = __builtin_amdgcn_exp2f(AB ? sc[kb][2 * t + 1] - m_run
+                                                       : fmaf(sc[kb][2 * t + 1], c_log2, -m_run));
             pk[kb][t] = pack2<BF16>(e0, e1);
             if constexpr (BF16) {
               tl += e0 + e1;
@@ -970,7 +987,7 @@ static int head_group_256(const FwdParams& p, int D, bool varlen) {
   return (!varlen && kv_bytes_head > (8LL << 20)) ? 2 : HEAD_GROUP;
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS, bool AB = false>
 static hipError_t launch_one(FwdParams p, int head_group, hipStream_t stream) {
   constexpr long long BM = 32 * NW / KS;
   const long long tiles = VARLEN ? (long long)p.S / BM + p.B : ((long long)p.S + BM - 1) / BM;
@@ -982,15 +999,23 @@ static hipError_t launch_one(FwdParams p, int head_group, hipStream_t stream) {
   }
   p.head_group = (int)(head_group < nbh ? head_group : nbh);
   const long long grid = tiles * nbh;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW, EXT, KS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, VARLEN, NW, EXT, KS, AB>), dim3((unsigned)grid),
                      dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 static hipError_t launch_nw(const FwdParams& p, const FwdTuning& t, hipStream_t stream) {
-  // The mask/bias variants run with 4-wave workgroups only.
+  // The mask/bias variants run with 4-wave workgroups, except ALiBi alone at
+  // D = 128 where the plain instances would take 8 waves on 256 rows: it runs
+  // on their ping-pong schedule (the bias adds 3 VALU per score to the softmax
+  // phases, which still fit beside the other wave's matrix phase).
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
+    if constexpr (D == 128) {
+      if (p.window == 0 && p.n_global == 0 && choose_shape(p, VARLEN, t) == Shape::W8) {
+        return launch_one<D, BF16, CAUSAL, VARLEN, 8, false, 1, true>(p, t.head_group, stream);
+      }
+    }
     return launch_one<D, BF16, CAUSAL, VARLEN, 4, true, 1>(p, t.head_group, stream);
   }
   switch (choose_shape(p, VARLEN, t)) {

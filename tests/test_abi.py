@@ -115,6 +115,30 @@ def test_ext_empty_problem_is_noop():
     assert call_ext(window=16, S=0) == 0
 
 
+def call_ext_tuned(window=0, n_global=0, alibi=P, tile_rows=256, head_group=0, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=2, S=128, D=128, causal=1, scale=0.125,
+             dtype=binding.ATTN_DTYPE_BF16, cu=None)
+    a.update(kw)
+    return binding.attn_fwd_ext_tuned_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                          a["S"], a["D"], a["causal"], a["scale"], a["dtype"],
+                                          a["cu"], window, n_global, alibi, tile_rows, head_group,
+                                          None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tile_rows=64), -5), (dict(tile_rows=512), -5), (dict(window=8), -5), (dict(n_global=1), -5),
+    (dict(alibi=None), -5), (dict(D=64), -5), (dict(head_group=-1), -2), (dict(alibi=P + 2), -8),
+    (dict(tile_rows=128, window=-1), -2), (dict(q=None), -1), (dict(scale=float("nan")), -4),
+])
+def test_ext_tuned_argument_errors(kw, code):
+    assert call_ext_tuned(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(S=0), dict(tile_rows=128, window=4, S=0), dict(B=0, S=7, cu=P)])
+def test_ext_tuned_empty_problems_are_noops(kw):
+    assert call_ext_tuned(**kw) == 0
+
+
 def call_dec(**kw):
     a = dict(q=P, k=P, v=P, sl=None, o=P, lse=None, B=2, H=4, Sq=1, S_max=4096, D=128, causal=0,
              scale=0.1, dtype=binding.ATTN_DTYPE_BF16, ns=0, ws=None, wsb=0)

@@ -18,12 +18,13 @@ pytestmark = pytest.mark.gpu
 REL_O = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
 
 
-def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=None, case=None):
+def run_check(qb, kb, vb, dtype, causal, scale, window, n_global, slopes, cu=None, case=None,
+              tile_rows=0):
     q, k, v = to_dev(qb, dtype), to_dev(kb, dtype), to_dev(vb, dtype)
     sl = None if slopes is None else torch.from_numpy(slopes).cuda()
     cud = None if cu is None else torch.from_numpy(cu).cuda()
     o, lse = binding.fwd(q, k, v, causal=causal, scale=scale, cu_seqlens=cud, window=window,
-                         n_global=n_global, alibi_slopes=sl)
+                         n_global=n_global, alibi_slopes=sl, tile_rows=tile_rows)
     torch.cuda.synchronize()
     f = [synth.bits_to_f64(x, dtype) for x in (qb, kb, vb)]
     oref, lref = attention(*f, causal=causal, scale=scale, cu_seqlens=cu, window=window,
@@ -68,6 +69,59 @@ def test_ext_packed(window, n_global, alibi, causal):
               synth.alibi_slopes(H) if alibi else None, cu=cu,
               case=f"mask variant packed H={H} D={D} bf16 causal={causal} window={window} "
                    f"global={n_global} alibi={alibi}")
+
+
+@pytest.mark.parametrize("S", [333, 600])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_alibi_pingpong_padded(S, causal, dtype):
+    """ALiBi alone on the 8-wave ping-pong kernel (256-row tiles forced through
+    attn_fwd_ext_tuned): several query and key tiles, ragged tails, against the oracle."""
+    B, H, D = 2, 3, 128
+    say(f"alibi ping-pong padded S={S} {dtype} causal={causal}")
+    qb, kb, vb = synth.normal_qkv((B, S, H, D), dtype, 4500 + S)
+    run_check(qb, kb, vb, dtype, causal, scale_of(D), 0, 0, synth.alibi_slopes(H), tile_rows=256,
+              case=f"alibi ping-pong B={B} H={H} S={S} D={D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alibi_pingpong_packed(causal):
+    lens = [1, 3, 0, 130, 257, 64, 200, 513]
+    cu = synth.cu_seqlens_of(lens)
+    T, H, D = int(cu[-1]), 2, 128
+    say(f"alibi ping-pong packed causal={causal}")
+    qb, kb, vb = synth.normal_qkv((T, H, D), "bf16", 4600)
+    run_check(qb, kb, vb, "bf16", causal, scale_of(D), 0, 0, synth.alibi_slopes(H), cu=cu,
+              tile_rows=256, case=f"alibi ping-pong packed H={H} D={D} bf16 causal={causal}")
+
+
+def test_alibi_layer_sampled():
+    """The LLaMA-shaped layer with ALiBi, B4 H32 S4096 D128 bf16 causal, as the library runs it
+    by itself (ping-pong kernel): 64 sampled rows of every (batch, head) against the oracle."""
+    cfg = synth.CONFIGS["llama"]
+    inp = synth.make_inputs(cfg)
+    slopes = synth.alibi_slopes(cfg.H)
+    say(f"alibi layer {cfg.describe()}")
+    q, k, v = (to_dev(x, cfg.dtype) for x in (inp.q, inp.k, inp.v))
+    o, lse = binding.fwd(q, k, v, causal=True, alibi_slopes=torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu().numpy()
+    eo = el = floor = 0.0
+    excess = -float("inf")
+    for b in range(cfg.B):
+        rows = synth.sampled_rows(cfg.S, 64, 4700 + b, must=(0, 1, 255, 256, cfg.S - 1))
+        f = [synth.bits_to_f64(x[b], cfg.dtype) for x in (inp.q, inp.k, inp.v)]
+        oref, lref = attention_rows(*f, rows, causal=True, scale=scale_of(cfg.D), alibi_slopes=slopes)
+        og = o[b][rows].float().numpy().astype(np.float64)
+        eo = max(eo, max_abs(og, oref))
+        el = max(el, max_abs(lse[b][:, rows], lref))
+        excess = max(excess, float((np.abs(og - oref)
+                                    - (TOL_O[cfg.dtype] + REL_O[cfg.dtype] * np.abs(oref))).max()))
+        floor = max(floor, rne_floor(oref, cfg.dtype))
+    say(f"    sampled max|dO|={eo:.3e} floor={floor:.3e} max|dLSE|={el:.3e} excess={excess:.3e}")
+    record(f"alibi layer {cfg.describe()} (64 sampled rows of every (b, h))", cfg.dtype, eo, el,
+           floor=floor, n_rows=64 * cfg.B * cfg.H, excess=excess)
+    assert excess <= 0.0 and el <= TOL_LSE
 
 
 def test_ext_zero_slopes_match_plain():
