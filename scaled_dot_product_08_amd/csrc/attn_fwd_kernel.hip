@@ -1008,7 +1008,7 @@ template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 static hipError_t launch_nw(const FwdParams& p, const FwdTuning& t, hipStream_t stream) {
   // The mask/bias variants run with 4-wave workgroups, except ALiBi alone at
   // D = 128 where the plain instances would take 8 waves on 256 rows: it runs
-  // on their ping-pong schedule (the bias adds 3 VALU per score to the softmax
+  // on their ping-pong schedule (the bias adds 2 VALU per score to the softmax
   // phases, which still fit beside the other wave's matrix phase).
   if (p.window > 0 || p.n_global > 0 || p.alibi != nullptr) {
     if constexpr (D == 128) {
