@@ -84,6 +84,17 @@ def render(d: dict, n_tests: int | None, source: str | None) -> str:
             out.append(f"| {g} | {len(cs)} | {rows} | {fmt(w['max_abs_dO'])} | {fmt(w.get('rne_floor_O'))} | "
                        f"causal{tail} | {fmt(max(ex)) if ex else '—'} | "
                        f"{fmt(max(c['max_abs_dLSE'] for c in cs))} |")
+    ab = [c for c in cases if c["case"].startswith("alibi ")]
+    if ab:
+        out += ["",
+                "## ALiBi alone on the 8-wave ping-pong kernel (same bound as the mask variants)",
+                "",
+                "| case | rows | max\\|ΔO\\| | floor | ΔO − bound | max\\|ΔLSE\\| |",
+                "|---|---|---|---|---|---|"]
+        for c in ab:
+            out.append(f"| {c['case']} | {c['rows_checked']} | {fmt(c['max_abs_dO'])} | "
+                       f"{fmt(c.get('rne_floor_O'))} | {fmt(c.get('worst_excess_over_bound'))} | "
+                       f"{fmt(c['max_abs_dLSE'])} |")
     return "\n".join(out) + "\n"
 
 
