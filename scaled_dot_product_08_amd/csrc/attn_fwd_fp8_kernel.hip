@@ -233,7 +233,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
           e[i] = __builtin_amdgcn_exp2f(fmaf(s[kb][r0 + i], c_log2, -m_sub));
           tl += e[i];
         }
-        uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        // The first conversion writes the low half and keeps the high half of
+        // its third operand, which the second overwrites: any register serves
+        // (a constant 0 there cost one v_mov per word).
+        uint32_t x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], __builtin_bit_cast(int, e[0]), false);
         x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], (int)x, true);
         pk[w] = x;
       }
