@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
     uint32_t pk[8];
     auto exps = [&](float m) {
       const float m_sub = m - P_SHIFT_LOG2;
-      float tl = 0.0f;
+      float tl = -0.0f;   // -0 + x folds to x
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2, r0 = 4 * (w & 3);

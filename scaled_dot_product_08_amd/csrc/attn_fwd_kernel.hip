@@ -464,7 +464,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
     // error below 2.5e-4 and sums the rounded pairs with one dot2.
     uint32_t pk[NKB][8];
     auto exps = [&](float m_sub) {
-      float tl = 0.0f;
+      float tl = BF16 ? -0.0f : 0.0f;   // -0 + x folds to x (bf16 sums fp32 adds)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
           m_run = half_max(mx) * c_log2;
         }
         if constexpr (AB) alibi_bias(sc, key0);      // scores now log2-scaled
-        float tl = 0.0f;
+        float tl = BF16 ? -0.0f : 0.0f;   // -0 + x folds to x (bf16 sums fp32 adds)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
