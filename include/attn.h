@@ -106,11 +106,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  *   head_group : how many (batch, head) pairs one XCD interleaves the query
  *                tiles of (clamped to B*H, or H when packed); 0 lets the
  *                library choose. Negative: ATTN_ERR_SHAPE.
- * Results do not depend on head_group. The launch shapes sum the keys of a
- * row in different groupings (D = 64 walks 128 keys per step with 4 waves on
- * 128 rows, 64 with 256 rows; the key split adds two partial sums), so they
- * agree to rounding, except that 128- and 256-row tiles without a key split
- * are bitwise identical for D = 128.
+ * Results do not depend on head_group. 128- and 256-row tiles without a key
+ * split are bitwise identical (both walk 64-key tiles with the same per-row
+ * arithmetic); the key split adds two partial sums, so it agrees with them to
+ * rounding.
  */
 int attn_fwd_tuned(const void* q, const void* k, const void* v, void* out, float* lse,
                    int B, int H, int S, int D, int causal, float scale, int dtype,

@@ -105,7 +105,7 @@ __device__ __forceinline__ float add_pair_f16(uint32_t p, float acc) {
 // AB: the ALiBi bias alone (no window, no global rows) on the ping-pong
 // schedule; the other mask variants take EXT (4 waves).
 template <int D, bool BF16, bool CAUSAL, bool VARLEN, int NW, bool EXT, int KS, bool AB = false>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4 && !EXT) ? 3 : 8 / NW) void attn_fwd_kernel(FwdParams p) {
   constexpr int NWAVES = NW;
   constexpr int NWR = NW / KS;                 // waves per key group (one per 32 query rows)
   constexpr int BM = 32 * NWR;                 // query rows per workgroup
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fwd_kernel(FwdParams p) 
   // 16 KB as 64 keys of D = 128, twice the matrix work per barrier and per
   // softmax pass; measured 2-7 % faster on B4 H12 S2048, 7 % slower with 8
   // waves on 256 rows), else 64.
-  constexpr int BN = (D == 64 && !EXT && NWR == 4) ? 128 : 64;
+  constexpr int BN = 64;
   constexpr int GBN = KS * BN;                 // keys per LDS tile (all groups)
   constexpr int NKB = BN / 32;                 // 32-key blocks per group block
   constexpr int ROWB = D * 2;                  // bytes per K/V row

@@ -211,11 +211,10 @@ def test_lse_optional():
 @pytest.mark.parametrize("name", ["llama", "mha_causal", "mha"])
 def test_tile_size_choice(name):
     """Workgroup shapes against each other. 128- and 256-row query tiles: bitwise identical O
-    and LSE for D = 128 (same per-row arithmetic over the same 64-key tiles). For D = 64 the
-    4-wave kernel walks 128-key tiles, and the key split adds two partial sums, so the lazy
-    maximum and the row sums are grouped differently: each result is within the oracle
-    tolerance, hence they differ by at most twice it (O) and by 5e-4 (LSE, twice the 2.5e-4
-    bound of the fp16 row sums)."""
+    and LSE (same per-row arithmetic over the same 64-key tiles). The key split adds two
+    partial sums, so its lazy maximum and row sums are grouped differently: each result is
+    within the oracle tolerance, hence they differ by at most twice it (O) and by 5e-4 (LSE,
+    twice the 2.5e-4 bound of the fp16 row sums)."""
     cfg = synth.CONFIGS[name]
     inp = synth.make_inputs(cfg, B=2 if cfg.B > 2 else cfg.B)
     outs = []
@@ -223,8 +222,7 @@ def test_tile_size_choice(name):
         o, lse = run_padded(inp.q, inp.k, inp.v, cfg.dtype, cfg.causal, scale_of(cfg.D),
                             shape=shape)
         outs.append((o.cpu(), lse.cpu()))
-    if cfg.D == 128:
-        assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
     for a in range(len(outs)):
         for b in range(a + 1, len(outs)):
             assert (outs[a][0].float() - outs[b][0].float()).abs().max().item() <= 2 * TOL_O[cfg.dtype]
