@@ -698,15 +698,29 @@ __global__ __launch_bounds__(NW * 64, (D == 64 && NW == 4 && !EXT) ? 3 : 8 / NW)
           }
           m_run = half_max(mx) * c_log2;
         }
-        if constexpr (AB) alibi_bias(sc, key0);      // scores now log2-scaled
+        if constexpr (AB && !CAUSAL) alibi_bias(sc, key0);      // scores now log2-scaled
+        // Under causality every key a row sees has j <= i, so its bias is
+        // slope * (j - i) with no absolute value, and the running maximum folds
+        // into the per-lane base: each exponent then takes two fused
+        // multiply-adds (masked scores stay -inf).
+        const float bm = (AB && CAUSAL) ? fmaf(slope2, (float)(key0 + hh * 4 - qi), -m_run) : 0.0f;
+        auto expo = [&](int kb, int r) __attribute__((always_inline)) {
+          if constexpr (AB && CAUSAL) {
+            const float w = fmaf(slope2, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), bm);
+            return __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c_log2, w));
+          } else if constexpr (AB) {
+            return __builtin_amdgcn_exp2f(sc[kb][r] - m_run);
+          } else {
+            return __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c_log2, -m_run));
+          }
+        };
         float tl = BF16 ? -0.0f : 0.0f;   // -0 + x folds to x (bf16 sums fp32 adds)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            const float e0 = __builtin_amdgcn_exp2f(AB ? sc[kb][2 * t] - m_run : fmaf(sc[kb][2 * t], c_log2, -m_run));
-            const float e1 = __builtin_amdgcn_exp2f(AB ? sc[kb][2 * t + 1] - m_run
-                                                       : fmaf(sc[kb][2 * t + 1], c_log2, -m_run));
+            const float e0 = expo(kb, 2 * t);
+            const float e1 = expo(kb, 2 * t + 1);
             pk[kb][t] = pack2<BF16>(e0, e1);
             if constexpr (BF16) {
               tl += e0 + e1;
