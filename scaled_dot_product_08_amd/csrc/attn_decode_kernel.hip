@@ -121,10 +121,25 @@ __global__ __launch_bounds__(NWAVE * 64) void attn_decode_split_kernel(DecodePar
   const int grp = lane / G::KL;       // which cache row of a wave-wide load
   const int sub = lane % G::KL;       // which 16-byte column chunk of that row
 
-  // Workgroup i runs on XCD i % 8; renumber so that each XCD owns a
-  // contiguous run of (row, split) items (the Sq query rows that share a
-  // split are neighbours, so their repeated cache reads meet in one L2).
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  // Workgroup i runs on XCD i % 8. With per-batch cache lengths, and when the
+  // (batch, head) pairs divide evenly among the XCDs, XCD x takes pairs x,
+  // x + 8, x + 16, ... with all their (split, query row) items: heads of one
+  // batch share its length, so every XCD then holds the same share of each
+  // batch's cache (exactly so when H is a multiple of 8), where contiguous
+  // runs of pairs would hand an XCD whole batches and so unequal amounts of
+  // cache. Otherwise (full caches: equal work per pair, and contiguous runs
+  // measured faster there) each XCD owns a contiguous run of items. Either
+  // way the Sq query rows that share a split are neighbours, so their
+  // repeated cache reads meet in one L2.
+  const int per_bh = p.n_splits * p.Sq;
+  const int n_bh = (int)gridDim.x / per_bh;
+  int logical;
+  if (p.seqlens != nullptr && n_bh % NXCD == 0) {
+    const int xcd = blockIdx.x % NXCD, local = blockIdx.x / NXCD;
+    logical = ((local / per_bh) * NXCD + xcd) * per_bh + local % per_bh;
+  } else {
+    logical = xcd_logical(blockIdx.x, gridDim.x);
+  }
   const int qi = logical % p.Sq;
   const int rest = logical / p.Sq;
   const int split = rest % p.n_splits;

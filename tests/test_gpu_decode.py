@@ -44,6 +44,7 @@ CASES = [
     (2, 4, 4, 2048, 64, [2048, 3]),
     (1, 7, 2, 129, 128, [129]),
     (5, 1, 1, 16, 128, [16, 0, 1, 15, 2]),
+    (3, 1, 8, 3000, 128, [3000, 1, 1777]),
 ]
 
 
